@@ -1,0 +1,181 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE feed-forward sublayer library.
+ *
+ * One call, moe_block_forward, runs the post-attention half of a GLM-style MoE
+ * block on one GPU:
+ *
+ *   h   = RMSNorm(x) * norm_w                    (fp32 math, cast back, gain)
+ *   s   = sigmoid(h . router_w^T)                (one score per routed expert)
+ *   sel = top_k experts by s + corr_bias         (bias used for selection only)
+ *   w_j = routed_scale * s_sel_j / sum_j s_sel_j
+ *   out = x + shared(h) + sum_j w_j * expert_sel_j(h)
+ *
+ * with every expert a SwiGLU MLP down(silu(gate h) * up h).
+ *
+ * Sources (web pages, cited by title and section):
+ *  - "GLM-5 · Input features" (OpenModelAtlas), excerpts "rmsnorm"
+ *    (GlmMoeDsaRMSNorm: float32 normalisation by the root mean square, cast back
+ *    to the input dtype, then the per-feature gain; epsilon default 1e-6),
+ *    "block" (GlmMoeDsaDecoderLayer: out = residual + mlp(norm(residual))) and
+ *    "mlp" (GlmMoeDsaMLP: the SwiGLU form, bias-free linear maps).
+ *  - "nemo_automodel ... glm4_moe.state_dict_adapter", Glm4MoeStateDictAdapter:
+ *    the grouped native expert layout gate_and_up_projs [n_experts, dim,
+ *    2*moe_inter_dim] and down_projs [n_experts, moe_inter_dim, dim], and the
+ *    shared expert's separate gate/up/down nn.Linear weights.
+ *  - "GLM-5 · MoE transformer block", Parameters table and note: one
+ *    correction-bias value per expert, held by the router as a buffer.
+ *  The router rule (sigmoid, bias for selection only, renormalised unbiased
+ *  scores times routed_scale) is not printed on the pages; it is the workload
+ *  definition this library implements.
+ *
+ * Conventions
+ *  - All tensors are row-major, contiguous, in device memory, 16-byte aligned.
+ *  - D = the plan's dtype (fp32 or bfloat16) for x, out, norm_w, router_w,
+ *    gate_up, down and shared_*; corr_bias is always fp32.
+ *  - Layouts (T = num_tokens, d = dim, E = n_experts, I = moe_inter,
+ *    Is = shared_inter, k = top_k):
+ *      x, out        [T, d]        D
+ *      norm_w        [d]           D
+ *      router_w      [E, d]        D   (nn.Linear [out, in])
+ *      corr_bias     [E]           fp32
+ *      gate_up       [E, d, 2I]    D   columns [0, I) gate, [I, 2I) up
+ *      down          [E, I, d]     D
+ *      shared_gate   [Is, d]       D   (nn.Linear [out, in])
+ *      shared_up     [Is, d]       D
+ *      shared_down   [d, Is]       D
+ *  - Ownership: the caller allocates and owns every tensor and the workspace.
+ *    The library never allocates device memory, frees, or synchronises inside
+ *    moe_block_forward.  A plan holds host memory only and is immutable after
+ *    creation, so one plan may serve several threads.  A workspace serves one
+ *    call in flight at a time; later calls on the same stream may reuse it.
+ *  - Aliasing: out may alias x (in-place residual); no other aliasing.
+ *  - Errors: arguments are validated synchronously before anything is
+ *    enqueued; on error nothing is written and a status is returned.  Device
+ *    faults surface at the caller's next synchronisation.  Inputs must be
+ *    finite; NaN/Inf behaviour is unspecified.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+typedef enum {
+  MOE_SUCCESS = 0,
+  MOE_ERROR_INVALID_VALUE = 1,       /* null pointer, bad size, top_k, num_tokens, scale */
+  MOE_ERROR_NOT_SUPPORTED = 2,       /* shape / dtype / path outside what the kernels handle */
+  MOE_ERROR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the plan's requirement */
+  MOE_ERROR_MISALIGNED = 4,          /* a pointer not 16-byte aligned */
+  MOE_ERROR_HIP = 5                  /* a HIP launch or copy returned an error */
+} moe_status_t;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
+
+/* Kernel family for the expert matmuls.
+ *  AUTO:   STREAM when the mean tokens per routed expert is small (decode-sized
+ *          batches, where the expert weights are streamed once from HBM), MFMA
+ *          otherwise.  fp32 plans always use STREAM.
+ *  STREAM: weight-streaming FMA kernels (any dtype).
+ *  MFMA:   LDS-tiled bf16 matrix-core kernels (bf16 only). */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_MFMA = 2 } moe_path_t;
+
+typedef struct {
+  uint32_t struct_size;  /* sizeof(moe_config_t) */
+  int32_t dim;           /* d: multiple of 64 */
+  int64_t max_tokens;    /* largest num_tokens a forward call may pass (>= 0) */
+  int32_t n_experts;     /* E: 1..1024 */
+  int32_t moe_inter;     /* I: multiple of 64 */
+  int32_t shared_inter;  /* Is: 0 (no shared expert) or a multiple of 64 */
+  int32_t max_top_k;     /* 1..min(E, 16) */
+  int32_t dtype;         /* moe_dtype_t */
+  int32_t path;          /* moe_path_t */
+  float eps;             /* RMSNorm epsilon (> 0) */
+  uint32_t flags;        /* reserved, must be 0 */
+} moe_config_t;
+
+typedef struct moe_plan* moe_plan_t;
+
+/* Validate *cfg and create a plan; *workspace_bytes receives the device
+ * workspace size every moe_block_forward call with this plan needs.
+ * Returns INVALID_VALUE for null pointers or out-of-range fields,
+ * NOT_SUPPORTED for shapes/dtypes/paths the kernels do not handle. */
+MOE_API moe_status_t moe_plan_create(const moe_config_t* cfg, moe_plan_t* plan, size_t* workspace_bytes);
+
+/* Destroy a plan (NULL is accepted). */
+MOE_API moe_status_t moe_plan_destroy(moe_plan_t plan);
+
+/* Enqueue the whole sublayer on `stream` (a hipStream_t; NULL = default stream).
+ * num_tokens in [0, max_tokens]; 0 is a successful no-op.  top_k in
+ * [1, min(E, max_top_k)].  routed_scale finite.  Shared pointers may be NULL
+ * only when the plan's shared_inter is 0.  Returns asynchronously. */
+MOE_API moe_status_t moe_block_forward(moe_plan_t plan, void* workspace, size_t workspace_bytes,
+                               void* stream, int64_t num_tokens, const void* x, const void* norm_w,
+                               const void* router_w, const float* corr_bias, const void* gate_up,
+                               const void* down, const void* shared_gate, const void* shared_up,
+                               const void* shared_down, int32_t top_k, float routed_scale,
+                               void* out);
+
+/* Copy the routing of the last forward call that used `workspace` into caller
+ * buffers (device memory), enqueued on `stream`:
+ *   topk_idx [num_tokens, top_k] int32  experts in (key desc, index asc) order
+ *   topk_w   [num_tokens, top_k] fp32   weights in the same order
+ *   counts   [E] int32                  tokens routed to each expert
+ * Any destination may be NULL.  num_tokens/top_k must be those of that call. */
+MOE_API moe_status_t moe_read_routing(moe_plan_t plan, const void* workspace, void* stream,
+                              int64_t num_tokens, int32_t top_k, int32_t* topk_idx, float* topk_w,
+                              int32_t* counts);
+
+/* Intermediate buffers of the last forward call (tests, diagnostics). */
+typedef enum {
+  MOE_BUF_H = 0,          /* [T, d] D: normalised input */
+  MOE_BUF_OFFSETS = 1,    /* [E + 1] int32: expert segment offsets in the permuted order */
+  MOE_BUF_PERM_TOKEN = 2, /* [T*k] int32: token of each permuted row */
+  MOE_BUF_ROW_OF = 3,     /* [T, k] int32: permuted row of assignment (t, j) */
+  MOE_BUF_ACT = 4,        /* [T*k, I] D: silu(gate) * up per permuted row */
+  MOE_BUF_Y = 5,          /* [T*k, d] D: routed expert output per permuted row */
+  MOE_BUF_SHARED_ACT = 6, /* [T, Is] D: shared expert silu(gate) * up */
+  MOE_BUF_COUNT = 7
+} moe_buffer_t;
+
+/* Copy intermediate buffer `which` of the last forward call into `dst` (device
+ * memory, dst_bytes >= the buffer's size for num_tokens/top_k), on `stream`. */
+MOE_API moe_status_t moe_read_buffer(moe_plan_t plan, const void* workspace, void* stream,
+                             int64_t num_tokens, int32_t top_k, int32_t which, void* dst,
+                             size_t dst_bytes);
+
+/* Size in bytes of intermediate buffer `which` for num_tokens/top_k (0 if invalid). */
+MOE_API size_t moe_buffer_bytes(moe_plan_t plan, int64_t num_tokens, int32_t top_k, int32_t which);
+
+/* Path the plan takes for num_tokens/top_k (MOE_PATH_STREAM or MOE_PATH_MFMA). */
+MOE_API int32_t moe_plan_path(moe_plan_t plan, int64_t num_tokens, int32_t top_k);
+
+/* Per-stage GPU timing.  When enabled on a plan, moe_block_forward records a
+ * HIP event before and after each kernel it enqueues; after the caller
+ * synchronises, moe_stage_times adds the elapsed milliseconds of every call
+ * since the last reset into ms[stage] and the number of calls into *calls.
+ * Stage names come from moe_stage_name.  Timing is meant for one thread. */
+#define MOE_MAX_STAGES 16
+MOE_API moe_status_t moe_set_stage_timing(moe_plan_t plan, int32_t enable);
+MOE_API moe_status_t moe_stage_times(moe_plan_t plan, double* ms /*[MOE_MAX_STAGES]*/, int64_t* calls);
+MOE_API const char* moe_stage_name(int32_t stage);
+
+MOE_API const char* moe_status_string(moe_status_t status);
+MOE_API int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

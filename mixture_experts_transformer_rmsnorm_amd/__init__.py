@@ -1,0 +1,274 @@
+"""MI355X (gfx950) MoE feed-forward sublayer: thin Python binding of ``include/moe.h``.
+
+Every step of the sublayer runs in the HIP kernels of ``libmoe_mi355x.so``; this
+module only marshals arguments (device pointers from torch tensors, the current
+HIP stream) and turns status codes into exceptions.  There is no fallback: if the
+library is missing, ``load()`` raises.
+
+Functions keep the C names: ``moe_plan_create``, ``moe_plan_destroy``,
+``moe_block_forward``, ``moe_read_routing``, ``moe_read_buffer``,
+``moe_buffer_bytes``, ``moe_plan_path``, ``moe_set_stage_timing``,
+``moe_stage_times``, ``moe_stage_name``, ``moe_status_string``,
+``moe_abi_version``.  ``MoEBlock`` bundles a plan, its workspace and the weights.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_SUCCESS = 0
+MOE_ERROR_INVALID_VALUE = 1
+MOE_ERROR_NOT_SUPPORTED = 2
+MOE_ERROR_WORKSPACE_TOO_SMALL = 3
+MOE_ERROR_MISALIGNED = 4
+MOE_ERROR_HIP = 5
+MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_MFMA = 0, 1, 2
+(MOE_BUF_H, MOE_BUF_OFFSETS, MOE_BUF_PERM_TOKEN, MOE_BUF_ROW_OF, MOE_BUF_ACT, MOE_BUF_Y,
+ MOE_BUF_SHARED_ACT) = range(7)
+MOE_MAX_STAGES = 16
+ABI_VERSION = 1
+
+EXPORTS = ("moe_plan_create", "moe_plan_destroy", "moe_block_forward", "moe_read_routing",
+           "moe_read_buffer", "moe_buffer_bytes", "moe_plan_path", "moe_set_stage_timing",
+           "moe_stage_times", "moe_stage_name", "moe_status_string", "moe_abi_version")
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (what or "moe", moe_status_string(status), status))
+
+
+class moe_config_t(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("dim", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int64), ("n_experts", ctypes.c_int32),
+                ("moe_inter", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
+                ("max_top_k", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("path", ctypes.c_int32), ("eps", ctypes.c_float), ("flags", ctypes.c_uint32)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise ImportError("libmoe_mi355x.so not found at %s; build it with "
+                              "mixture_experts_transformer_rmsnorm_amd/build.py" % path)
+        lib = ctypes.CDLL(path)
+        P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        lib.moe_plan_create.argtypes = [ctypes.POINTER(moe_config_t), ctypes.POINTER(P),
+                                        ctypes.POINTER(ctypes.c_size_t)]
+        lib.moe_plan_destroy.argtypes = [P]
+        lib.moe_block_forward.argtypes = [P, P, ctypes.c_size_t, P, i64, P, P, P, P, P, P, P, P, P,
+                                          i32, ctypes.c_float, P]
+        lib.moe_read_routing.argtypes = [P, P, P, i64, i32, P, P, P]
+        lib.moe_read_buffer.argtypes = [P, P, P, i64, i32, i32, P, ctypes.c_size_t]
+        lib.moe_buffer_bytes.argtypes = [P, i64, i32, i32]
+        lib.moe_buffer_bytes.restype = ctypes.c_size_t
+        lib.moe_plan_path.argtypes = [P, i64, i32]
+        lib.moe_plan_path.restype = i32
+        lib.moe_set_stage_timing.argtypes = [P, i32]
+        lib.moe_stage_times.argtypes = [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+        lib.moe_stage_name.argtypes = [i32]
+        lib.moe_stage_name.restype = ctypes.c_char_p
+        lib.moe_status_string.argtypes = [i32]
+        lib.moe_status_string.restype = ctypes.c_char_p
+        lib.moe_abi_version.argtypes = []
+        lib.moe_abi_version.restype = i32
+        for fn in ("moe_plan_create", "moe_plan_destroy", "moe_block_forward", "moe_read_routing",
+                   "moe_read_buffer", "moe_set_stage_timing", "moe_stage_times"):
+            getattr(lib, fn).restype = i32
+        if lib.moe_abi_version() != ABI_VERSION:
+            raise ImportError("libmoe_mi355x.so ABI %d != binding ABI %d"
+                              % (lib.moe_abi_version(), ABI_VERSION))
+        _lib = lib
+        return lib
+
+
+def _ptr(t):
+    """Device pointer of a tensor (or an int / None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status, what):
+    if status != MOE_SUCCESS:
+        raise MoEError(status, what)
+
+
+# ----------------------------------------------------------------------------- C names
+def moe_status_string(status: int) -> str:
+    s = load().moe_status_string(status)
+    return s.decode() if s else "unknown status"
+
+
+def moe_abi_version() -> int:
+    return load().moe_abi_version()
+
+
+def moe_stage_name(stage: int):
+    s = load().moe_stage_name(stage)
+    return s.decode() if s else None
+
+
+def make_config(dim, max_tokens, n_experts, moe_inter, shared_inter, max_top_k, dtype="bf16",
+                path=MOE_PATH_AUTO, eps=1e-6, flags=0) -> moe_config_t:
+    dt = {"f32": MOE_DTYPE_F32, "bf16": MOE_DTYPE_BF16}.get(dtype, dtype)
+    return moe_config_t(ctypes.sizeof(moe_config_t), dim, max_tokens, n_experts, moe_inter,
+                        shared_inter, max_top_k, dt, path, eps, flags)
+
+
+def moe_plan_create(cfg: moe_config_t):
+    """Returns (plan handle, workspace bytes)."""
+    plan = ctypes.c_void_p()
+    ws = ctypes.c_size_t()
+    _check(load().moe_plan_create(ctypes.byref(cfg), ctypes.byref(plan), ctypes.byref(ws)),
+           "moe_plan_create")
+    return plan.value, ws.value
+
+
+def moe_plan_destroy(plan) -> None:
+    _check(load().moe_plan_destroy(plan), "moe_plan_destroy")
+
+
+def moe_block_forward(plan, workspace, workspace_bytes, stream, num_tokens, x, norm_w, router_w,
+                      corr_bias, gate_up, down, shared_gate, shared_up, shared_down, top_k,
+                      routed_scale, out) -> None:
+    _check(load().moe_block_forward(
+        plan, _ptr(workspace), workspace_bytes, _stream(stream), num_tokens, _ptr(x),
+        _ptr(norm_w), _ptr(router_w), _ptr(corr_bias), _ptr(gate_up), _ptr(down),
+        _ptr(shared_gate), _ptr(shared_up), _ptr(shared_down), top_k, routed_scale, _ptr(out)),
+        "moe_block_forward")
+
+
+def moe_read_routing(plan, workspace, stream, num_tokens, top_k, topk_idx=None, topk_w=None,
+                     counts=None) -> None:
+    _check(load().moe_read_routing(plan, _ptr(workspace), _stream(stream), num_tokens, top_k,
+                                   _ptr(topk_idx), _ptr(topk_w), _ptr(counts)),
+           "moe_read_routing")
+
+
+def moe_buffer_bytes(plan, num_tokens, top_k, which) -> int:
+    return load().moe_buffer_bytes(plan, num_tokens, top_k, which)
+
+
+def moe_read_buffer(plan, workspace, stream, num_tokens, top_k, which, dst, dst_bytes) -> None:
+    _check(load().moe_read_buffer(plan, _ptr(workspace), _stream(stream), num_tokens, top_k,
+                                  which, _ptr(dst), dst_bytes), "moe_read_buffer")
+
+
+def moe_plan_path(plan, num_tokens, top_k) -> int:
+    return load().moe_plan_path(plan, num_tokens, top_k)
+
+
+def moe_set_stage_timing(plan, enable: bool) -> None:
+    _check(load().moe_set_stage_timing(plan, 1 if enable else 0), "moe_set_stage_timing")
+
+
+def moe_stage_times(plan):
+    """Returns ({stage name: total ms}, calls) accumulated since the last read."""
+    ms = (ctypes.c_double * MOE_MAX_STAGES)()
+    calls = ctypes.c_int64()
+    _check(load().moe_stage_times(plan, ms, ctypes.byref(calls)), "moe_stage_times")
+    out = {}
+    for i in range(MOE_MAX_STAGES):
+        name = moe_stage_name(i)
+        if name is not None:
+            out[name] = ms[i]
+    return out, calls.value
+
+
+# ----------------------------------------------------------------------------- convenience
+class MoEBlock:
+    """A plan, its device workspace and the sublayer's weights (torch tensors).
+
+    weights: dict with norm_w, router_w, corr_bias, gate_up, down and, when
+    shared_inter > 0, shared_gate, shared_up, shared_down, in the layouts of
+    ``include/moe.h``.
+    """
+
+    def __init__(self, weights: dict, max_tokens: int, top_k: int, routed_scale: float,
+                 eps: float = 1e-6, path: int = MOE_PATH_AUTO, device=None):
+        import torch
+        gu = weights["gate_up"]
+        E, d, I2 = gu.shape
+        sg = weights.get("shared_gate")
+        Is = 0 if sg is None else sg.shape[0]
+        self.dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}[gu.dtype]
+        self.weights = weights
+        self.top_k, self.routed_scale = top_k, routed_scale
+        self.dim, self.n_experts, self.moe_inter, self.shared_inter = d, E, I2 // 2, Is
+        self.cfg = make_config(d, max_tokens, E, I2 // 2, Is, top_k, self.dtype, path, eps)
+        self.plan, self.workspace_bytes = moe_plan_create(self.cfg)
+        self.workspace = torch.empty(max(self.workspace_bytes, 1), dtype=torch.uint8,
+                                     device=device or gu.device)
+
+    def close(self):
+        if self.plan:
+            moe_plan_destroy(self.plan)
+            self.plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def forward(self, x, out=None, stream=None):
+        """x: [..., d] tensor; returns out of the same shape (may be x itself)."""
+        import torch
+        shape = x.shape
+        x2 = x.reshape(-1, self.dim)
+        if not x2.is_contiguous():
+            raise ValueError("x must be contiguous")
+        if out is None:
+            out = torch.empty_like(x2)
+        w = self.weights
+        moe_block_forward(self.plan, self.workspace, self.workspace_bytes, stream, x2.shape[0], x2,
+                          w["norm_w"], w["router_w"], w["corr_bias"], w["gate_up"], w["down"],
+                          w.get("shared_gate"), w.get("shared_up"), w.get("shared_down"),
+                          self.top_k, self.routed_scale, out)
+        return out.reshape(shape)
+
+    __call__ = forward
+
+    def routing(self, num_tokens, stream=None):
+        """(topk_idx int32 [T, k], topk_w fp32 [T, k], counts int32 [E]) of the last call."""
+        import torch
+        dev = self.workspace.device
+        idx = torch.empty((num_tokens, self.top_k), dtype=torch.int32, device=dev)
+        wts = torch.empty((num_tokens, self.top_k), dtype=torch.float32, device=dev)
+        cnt = torch.empty((self.n_experts,), dtype=torch.int32, device=dev)
+        moe_read_routing(self.plan, self.workspace, stream, num_tokens, self.top_k, idx, wts, cnt)
+        return idx, wts, cnt
+
+    def buffer(self, which, num_tokens, stream=None):
+        """Intermediate buffer `which` (MOE_BUF_*) of the last call as a flat uint8 tensor."""
+        import torch
+        n = moe_buffer_bytes(self.plan, num_tokens, self.top_k, which)
+        dst = torch.empty(max(n, 1), dtype=torch.uint8, device=self.workspace.device)
+        moe_read_buffer(self.plan, self.workspace, stream, num_tokens, self.top_k, which, dst, n)
+        return dst[:n]

@@ -1,0 +1,361 @@
+// bf16 matrix-core (MFMA) kernels for gfx950: the grouped expert matmuls of
+// prefill-sized batches and the dense K-contiguous products (router logits,
+// shared expert).
+//
+// Tile: 128 (rows) x 128 (B columns) x 64 (K) per 256-thread block, four
+// wavefronts in a 2 x 2 arrangement, each owning 64 rows x 64 B-columns as
+// 4 x 4 tiles of v_mfma_f32_16x16x32_bf16 (fp32 accumulation).  A and B tiles
+// are staged in LDS with K contiguous (row stride 72 elements, so the 16-byte
+// fragment reads of 16 consecutive rows hit distinct banks) and double
+// buffered: the global loads of K-tile t+1 are in flight while tile t is
+// multiplied.
+//
+// B layouts:
+//  - K-contiguous ([N, K], nn.Linear weights: router, shared expert) is copied
+//    to LDS as is.
+//  - N-contiguous ([K, N], the grouped expert layout of
+//    Glm4MoeStateDictAdapter: gate_and_up_projs [E, d, 2I], down_projs
+//    [E, I, d]) is read with 16-byte row loads (4 rows x 8 columns per thread)
+//    and transposed in registers before the LDS store, so the fragment reads
+//    stay 16-byte vector reads.
+// The gate_up tile pairs gate columns [c, c+64) with up columns [I+c, I+c+64)
+// so that silu(gate) * up is formed in registers ("GLM-5 · Input features",
+// excerpt mlp).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int BM = kMfmaBM, BN = kMfmaBN, BK = kMfmaBK;
+constexpr int LDK = BK + 8;  // LDS row stride in elements (144 bytes)
+constexpr int kTileElems = BM * LDK;
+
+enum Epi { kEpiPartialF32 = 0, kEpiSwiGLU = 1, kEpiStore = 2 };
+
+struct MfmaProblem {
+  // A rows (K-contiguous): dense rows m, or grouped permuted rows gathered
+  // through a_gather (A row = a_gather[permuted row]) or taken directly.
+  const uint16_t* A;
+  int64_t lda;
+  const int32_t* a_gather;
+  // B, K-contiguous: row n at B1 + n*ldb (n < n_split) else B2 + (n-n_split)*ldb.
+  const uint16_t* B1;
+  const uint16_t* B2;
+  int64_t ldb;
+  int n_split;
+  // B, N-contiguous grouped: element (k, n) of expert e at Bg + e*b_stride + k*ldb + n;
+  // SwiGLU up columns start at column up_off.
+  const uint16_t* Bg;
+  int64_t b_stride;
+  int up_off;
+  int K;
+  int N;  // output columns (SwiGLU: number of act columns)
+  // grouped problems
+  const int2* mtiles;
+  const RouteHeader* hdr;
+  const int32_t* offsets;
+  const int32_t* counts;
+  // dense problems
+  int M;
+  int kt_per_split;
+  // output
+  void* C;
+  int64_t ldc;
+};
+
+__device__ __forceinline__ int b_local_col(int f, int wn) {
+  // B-columns of wave column wn: [wn*32, wn*32+32) and [64+wn*32, 64+wn*32+32)
+  return (f < 2 ? wn * 32 + f * 16 : 64 + wn * 32 + (f - 2) * 16);
+}
+
+__device__ __forceinline__ uint32_t sel_lo(uint32_t a, uint32_t b) {
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t sel_hi(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xffff0000u);
+}
+__device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+template <bool NN, int EPI>
+__global__ __launch_bounds__(256) void mfma_kernel(MfmaProblem p) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2 * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2 * kTileElems];
+  constexpr bool kGrouped = NN;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int n_tile = blockIdx.x;
+
+  int rows, seg = 0, m0, e = 0;
+  if (kGrouped) {
+    const int mt = blockIdx.y;
+    if (mt >= p.hdr->n_mtiles) return;
+    const int2 tt = p.mtiles[mt];
+    e = tt.x;
+    m0 = tt.y;
+    seg = p.offsets[e];
+    rows = min(BM, p.counts[e] - m0);
+  } else {
+    m0 = blockIdx.y * BM;
+    rows = min(BM, p.M - m0);
+  }
+  const int nkt = p.K / BK;
+  const int kt0 = kGrouped ? 0 : blockIdx.z * p.kt_per_split;
+  const int kt1 = kGrouped ? nkt : min(nkt, kt0 + p.kt_per_split);
+
+  // ---- per-thread global load assignments
+  // A: rows tid/8 + 32*i, 16-byte chunk tid%8
+  const uint16_t* a_src[4];
+  bool a_ok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = tid / 8 + 32 * i;
+    a_ok[i] = r < rows;
+    int64_t arow = 0;
+    if (a_ok[i]) {
+      if (kGrouped) {
+        const int64_t prow = seg + m0 + r;
+        arow = p.a_gather ? (int64_t)p.a_gather[prow] : prow;
+      } else {
+        arow = m0 + r;
+      }
+    }
+    a_src[i] = p.A + arow * p.lda + (tid % 8) * 8;
+  }
+  // B
+  const uint16_t* b_src[4];
+  bool b_ok[4];
+  int64_t b_kstride = 0;
+  if (!NN) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int lc = tid / 8 + 32 * i;
+      const int n = n_tile * BN + lc;
+      b_ok[i] = n < p.N;
+      const int nn = b_ok[i] ? n : 0;
+      const uint16_t* row = nn < p.n_split ? p.B1 + (int64_t)nn * p.ldb
+                                           : p.B2 + (int64_t)(nn - p.n_split) * p.ldb;
+      b_src[i] = row + (tid % 8) * 8;
+    }
+  } else {
+    // 4 consecutive k-rows (kg*4 ..) x 8 columns (ng*8 ..) per thread
+    const int ng = tid % 16, kg = tid / 16;
+    const int lc = ng * 8;
+    int gcol;
+    bool ok;
+    if (EPI == kEpiSwiGLU) {
+      const int c = n_tile * 64 + (lc & 63);
+      ok = c < p.N;
+      gcol = (lc < 64 ? 0 : p.up_off) + c;
+    } else {
+      gcol = n_tile * BN + lc;
+      ok = gcol < p.N;
+    }
+    const uint16_t* base = p.Bg + (int64_t)e * p.b_stride + (int64_t)(kg * 4) * p.ldb + (ok ? gcol : 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      b_ok[i] = ok;
+      b_src[i] = base + (int64_t)i * p.ldb;
+    }
+    b_kstride = (int64_t)BK * p.ldb;
+  }
+
+  uint4 ra[4], rb[4];
+  auto gload = [&](int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ra[i] = a_ok[i] ? ldg16(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
+    if (!NN) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rb[i] = b_ok[i] ? ldg16(b_src[i] + k0) : make_uint4(0, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        rb[i] = b_ok[i] ? ldg16(b_src[i] + (int64_t)kt * b_kstride) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint16_t* as = As + buf * kTileElems;
+    uint16_t* bs = Bs + buf * kTileElems;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(as + (tid / 8 + 32 * i) * LDK + (tid % 8) * 8) = ra[i];
+    if (!NN) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4*>(bs + (tid / 8 + 32 * i) * LDK + (tid % 8) * 8) = rb[i];
+    } else {
+      const int ng = tid % 16, kg = tid / 16;
+      // rb[r] holds row kg*4+r, columns ng*8 .. ng*8+7; write column c as 4 k-values
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int dw = c >> 1;
+        uint32_t lo, hi;
+        if (c & 1) {
+          lo = sel_hi(u4_get(rb[0], dw), u4_get(rb[1], dw));
+          hi = sel_hi(u4_get(rb[2], dw), u4_get(rb[3], dw));
+        } else {
+          lo = sel_lo(u4_get(rb[0], dw), u4_get(rb[1], dw));
+          hi = sel_lo(u4_get(rb[2], dw), u4_get(rb[3], dw));
+        }
+        *reinterpret_cast<uint2*>(bs + (ng * 8 + c) * LDK + kg * 4) = make_uint2(lo, hi);
+      }
+    }
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (kt0 < kt1) {
+    gload(kt0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const int buf = (kt - kt0) & 1;
+      if (kt + 1 < kt1) gload(kt + 1);
+      const uint16_t* as = As + buf * kTileElems;
+      const uint16_t* bs = Bs + buf * kTileElems;
+#pragma unroll
+      for (int ks = 0; ks < BK / 32; ++ks) {
+        const int kof = ks * 32 + (lane >> 4) * 8;
+        bf16x8_t af[4], bf[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+          af[mi] = *reinterpret_cast<const bf16x8_t*>(as + (wm * 64 + mi * 16 + (lane & 15)) * LDK + kof);
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          bf[f] = *reinterpret_cast<const bf16x8_t*>(bs + (b_local_col(f, wn) + (lane & 15)) * LDK + kof);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int f = 0; f < 4; ++f)
+            acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bf[f], acc[mi][f], 0, 0, 0);
+      }
+      if (kt + 1 < kt1) lstore(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: lane holds rows (lane/16)*4 + i, column lane%16 of each 16x16 tile
+  const int col16 = lane & 15;
+  if (EPI == kEpiPartialF32) {
+    float* out = (float*)p.C + (int64_t)blockIdx.z * p.M * p.N;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int n = n_tile * BN + b_local_col(f, wn) + col16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = wm * 64 + mi * 16 + (lane >> 4) * 4 + i;
+          if (r < rows && n < p.N) out[(int64_t)(m0 + r) * p.N + n] = acc[mi][f][i];
+        }
+      }
+  } else if (EPI == kEpiSwiGLU) {
+    uint16_t* out = (uint16_t*)p.C;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int c = n_tile * 64 + wn * 32 + f * 16 + col16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = wm * 64 + mi * 16 + (lane >> 4) * 4 + i;
+          if (r < rows && c < p.N) {
+            const float v = silu(acc[mi][f][i]) * acc[mi][f + 2][i];
+            out[(int64_t)(seg + m0 + r) * p.ldc + c] = (uint16_t)f32_to_bf16_bits(v);
+          }
+        }
+      }
+  } else {
+    uint16_t* out = (uint16_t*)p.C;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int c = n_tile * BN + b_local_col(f, wn) + col16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = wm * 64 + mi * 16 + (lane >> 4) * 4 + i;
+          if (r < rows && c < p.N)
+            out[(int64_t)(seg + m0 + r) * p.ldc + c] = (uint16_t)f32_to_bf16_bits(acc[mi][f][i]);
+        }
+      }
+  }
+}
+
+hipError_t launch_mfma_nt(const NtArgs& a, hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  MfmaProblem p = {};
+  p.A = (const uint16_t*)a.A;
+  p.lda = a.lda;
+  p.B1 = (const uint16_t*)a.B1;
+  p.B2 = (const uint16_t*)a.B2;
+  p.ldb = a.ldb;
+  p.n_split = a.n_split;
+  p.K = a.K;
+  p.N = a.N;
+  p.M = a.M;
+  p.kt_per_split = a.k_tiles_per_split;
+  p.C = a.out;
+  dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, a.splits);
+  mfma_kernel<false, kEpiPartialF32><<<grid, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_gate_up(const GroupArgs& g, int max_mtiles, const void* h,
+                               const void* gate_up, void* act, hipStream_t s) {
+  if (max_mtiles == 0) return hipSuccess;
+  MfmaProblem p = {};
+  p.A = (const uint16_t*)h;
+  p.lda = g.d;
+  p.a_gather = g.perm_token;
+  p.Bg = (const uint16_t*)gate_up;
+  p.ldb = 2 * (int64_t)g.I;
+  p.b_stride = (int64_t)g.d * 2 * g.I;
+  p.up_off = g.I;
+  p.K = g.d;
+  p.N = g.I;
+  p.mtiles = g.mtiles;
+  p.hdr = g.hdr;
+  p.offsets = g.offsets;
+  p.counts = g.counts;
+  p.C = act;
+  p.ldc = g.I;
+  dim3 grid((g.I + 63) / 64, max_mtiles);
+  mfma_kernel<true, kEpiSwiGLU><<<grid, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_down(const GroupArgs& g, int max_mtiles, const void* act, const void* down,
+                            void* y, hipStream_t s) {
+  if (max_mtiles == 0) return hipSuccess;
+  MfmaProblem p = {};
+  p.A = (const uint16_t*)act;
+  p.lda = g.I;
+  p.a_gather = nullptr;
+  p.Bg = (const uint16_t*)down;
+  p.ldb = g.d;
+  p.b_stride = (int64_t)g.I * g.d;
+  p.K = g.I;
+  p.N = g.d;
+  p.mtiles = g.mtiles;
+  p.hdr = g.hdr;
+  p.offsets = g.offsets;
+  p.counts = g.counts;
+  p.C = y;
+  p.ldc = g.d;
+  dim3 grid((g.d + BN - 1) / BN, max_mtiles);
+  mfma_kernel<true, kEpiStore><<<grid, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

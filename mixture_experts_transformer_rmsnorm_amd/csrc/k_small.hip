@@ -1,0 +1,426 @@
+// Bandwidth- and latency-bound kernels of the MoE sublayer for gfx950:
+// RMSNorm, the fp32 FMA GEMM (router / shared expert of fp32 plans), router
+// top-k, the permutation (chunk scan, expert scan, scatter), the shared-expert
+// SwiGLU finalisation and the weighted combine with the residual.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// RMSNorm ("GLM-5 · Input features", excerpt rmsnorm: fp32 normalisation by the
+// root mean square over the feature dimension, no centring, cast back to the
+// input dtype, then the per-feature gain).  One 256-thread block per row.
+// The mean of squares is accumulated in fp64 and rounded once to fp32; sqrt
+// and the reciprocal are evaluated in fp64 and rounded once, which gives
+// exactly the IEEE fp32 sqrt and divide.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x,
+                                                      const T* __restrict__ w, T* __restrict__ h,
+                                                      int d, float eps) {
+  constexpr int V = Elem<T>::kVec;
+  const int64_t row = blockIdx.x;
+  const T* xr = x + row * d;
+  const int nvec = d / V;
+  double ss = 0.0;
+  for (int i = threadIdx.x; i < nvec; i += blockDim.x) {
+    float f[V];
+    Elem<T>::unpack(ldg16(xr + (int64_t)i * V), f);
+#pragma unroll
+    for (int q = 0; q < V; ++q) ss += (double)f[q] * (double)f[q];
+  }
+  ss = wave_sum(ss);
+  __shared__ double red[4];
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  if (lane == 0) red[wid] = ss;
+  __syncthreads();
+  const double tot = red[0] + red[1] + red[2] + red[3];
+  const float ms = (float)(tot / (double)d);
+  const float den = ms + eps;
+  const float sq = (float)sqrt((double)den);
+  const float r = (float)(1.0 / (double)sq);
+  T* hr = h + row * d;
+  for (int i = threadIdx.x; i < nvec; i += blockDim.x) {
+    float f[V], g[V];
+    Elem<T>::unpack(ldg16(xr + (int64_t)i * V), f);
+    Elem<T>::unpack(ldg16(w + (int64_t)i * V), g);
+#pragma unroll
+    for (int q = 0; q < V; ++q) f[q] = Elem<T>::round(g[q] * Elem<T>::round(f[q] * r));
+    stg16(hr + (int64_t)i * V, Elem<T>::pack(f));
+  }
+}
+
+hipError_t launch_rmsnorm(int dtype, const void* x, const void* w, void* h, int64_t T, int d,
+                          float eps, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (dtype == kBF16)
+    rmsnorm_kernel<bf16><<<dim3((unsigned)T), 256, 0, s>>>((const bf16*)x, (const bf16*)w,
+                                                           (bf16*)h, d, eps);
+  else
+    rmsnorm_kernel<float><<<dim3((unsigned)T), 256, 0, s>>>((const float*)x, (const float*)w,
+                                                            (float*)h, d, eps);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// out[z][m][n] = sum over split z of A[m][k] * B[n][k] (both K-contiguous), fp32
+// accumulation.  32x32 output tile per 256-thread block, 2x2 outputs per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void fma_nt_kernel(NtArgs a) {
+  __shared__ float As[kFmaTile][kFmaTile + 1];
+  __shared__ float Bs[kFmaTile][kFmaTile + 1];
+  const int tid = threadIdx.x;
+  const int m0 = blockIdx.y * kFmaTile, n0 = blockIdx.x * kFmaTile, z = blockIdx.z;
+  const int nkt = a.K / kFmaTile;
+  const int kt0 = z * a.k_tiles_per_split;
+  const int kt1 = min(nkt, kt0 + a.k_tiles_per_split);
+  const T* A = (const T*)a.A;
+  const int ty = tid / 16, tx = tid % 16;
+  float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int k0 = kt * kFmaTile;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i, r = e / kFmaTile, c = e % kFmaTile;
+      const int m = m0 + r, n = n0 + r;
+      As[c][r] = (m < a.M) ? Elem<T>::load1(A, (int64_t)m * a.lda + k0 + c) : 0.f;
+      float bv = 0.f;
+      if (n < a.N) {
+        const T* Brow = n < a.n_split ? (const T*)a.B1 + (int64_t)n * a.ldb
+                                      : (const T*)a.B2 + (int64_t)(n - a.n_split) * a.ldb;
+        bv = Elem<T>::load1(Brow, k0 + c);
+      }
+      Bs[c][r] = bv;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < kFmaTile; ++kk) {
+      const float a0 = As[kk][ty * 2], a1 = As[kk][ty * 2 + 1];
+      const float b0 = Bs[kk][tx * 2], b1 = Bs[kk][tx * 2 + 1];
+      acc[0][0] += a0 * b0;
+      acc[0][1] += a0 * b1;
+      acc[1][0] += a1 * b0;
+      acc[1][1] += a1 * b1;
+    }
+    __syncthreads();
+  }
+  float* out = a.out + (int64_t)z * a.M * a.N;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int m = m0 + ty * 2 + i, n = n0 + tx * 2 + j;
+      if (m < a.M && n < a.N) out[(int64_t)m * a.N + n] = acc[i][j];
+    }
+}
+
+hipError_t launch_fma_nt(int dtype, const NtArgs& a, hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  dim3 grid((a.N + kFmaTile - 1) / kFmaTile, (a.M + kFmaTile - 1) / kFmaTile, a.splits);
+  if (dtype == kBF16)
+    fma_nt_kernel<bf16><<<grid, 256, 0, s>>>(a);
+  else
+    fma_nt_kernel<float><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Router selection.  One wavefront per token: lane l holds experts l, l+64, ...
+// score = sigmoid(logit) in fp32; key = score + corr_bias (fp32) decides the
+// selection; k rounds of a wave-wide arg-max over (key desc, expert asc); the
+// weights are the selected unbiased scores renormalised to sum routed_scale.
+// Each block also writes its chunk's per-expert histogram.
+constexpr int kTopkMaxQ = 16;  // experts per lane: E <= 1024
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ part, int splits,
+                                                   const float* __restrict__ bias, int64_t T,
+                                                   int E, int k, float rs,
+                                                   int32_t* __restrict__ idx_out,
+                                                   float* __restrict__ w_out,
+                                                   int32_t* __restrict__ chunk_cnt) {
+  __shared__ int hist[1024];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int nq = (E + kWave - 1) / kWave;
+  const int64_t tbase = (int64_t)blockIdx.x * kChunkTokens;
+  for (int tl = wid; tl < kChunkTokens; tl += 4) {
+    const int64_t t = tbase + tl;
+    if (t >= T) break;
+    float key[kTopkMaxQ], sc[kTopkMaxQ];
+#pragma unroll
+    for (int q = 0; q < kTopkMaxQ; ++q) {
+      const int e = lane + kWave * q;
+      key[q] = -INFINITY;
+      sc[q] = 0.f;
+      if (q < nq && e < E) {
+        float l = 0.f;
+        for (int z = 0; z < splits; ++z) l += part[((int64_t)z * T + t) * E + e];
+        const float sg = 1.0f / (1.0f + expf(-l));
+        sc[q] = sg;
+        key[q] = sg + bias[e];
+      }
+    }
+    uint32_t taken = 0;
+    float ssum = 0.f, my_s = 0.f;
+    int my_e = 0;
+    for (int j = 0; j < k; ++j) {
+      float bv = -INFINITY, bs = 0.f;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int q = 0; q < kTopkMaxQ; ++q) {
+        const int e = lane + kWave * q;
+        const bool ok = q < nq && e < E && !((taken >> q) & 1u);
+        if (ok && (key[q] > bv || (key[q] == bv && e < be))) {
+          bv = key[q];
+          be = e;
+          bs = sc[q];
+        }
+      }
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, kWave);
+        const int oe = __shfl_xor(be, off, kWave);
+        const float os = __shfl_xor(bs, off, kWave);
+        if (ov > bv || (ov == bv && oe < be)) {
+          bv = ov;
+          be = oe;
+          bs = os;
+        }
+      }
+      if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
+      ssum += bs;
+      if (lane == j) {
+        my_s = bs;
+        my_e = be;
+      }
+      if (lane == 0) atomicAdd(&hist[be], 1);
+    }
+    if (lane < k) {
+      idx_out[t * k + lane] = my_e;
+      w_out[t * k + lane] = rs * my_s / ssum;
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) chunk_cnt[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+hipError_t launch_topk(const float* logit_part, int splits, const float* corr_bias, int64_t T,
+                       int E, int k, float routed_scale, int32_t* topk_idx, float* topk_w,
+                       int32_t* chunk_cnt, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int64_t nchunks = (T + kChunkTokens - 1) / kChunkTokens;
+  topk_kernel<<<dim3((unsigned)nchunks), 256, 0, s>>>(logit_part, splits, corr_bias, T, E, k,
+                                                      routed_scale, topk_idx, topk_w, chunk_cnt);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Permutation, step 1: per expert, exclusive prefix of the chunk histograms over
+// chunks (in place) and the expert's total.  One wavefront per expert.
+__global__ __launch_bounds__(256) void scan_chunks_kernel(int32_t* __restrict__ chunk_cnt,
+                                                          int nchunks, int E,
+                                                          int32_t* __restrict__ counts) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int e = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (e >= E) return;
+  int carry = 0;
+  for (int c0 = 0; c0 < nchunks; c0 += kWave) {
+    const int c = c0 + lane;
+    const int v = c < nchunks ? chunk_cnt[(int64_t)c * E + e] : 0;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int o = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += o;
+    }
+    if (c < nchunks) chunk_cnt[(int64_t)c * E + e] = carry + incl - v;
+    carry += __shfl(incl, kWave - 1, kWave);
+  }
+  if (lane == 0) counts[e] = carry;
+}
+
+// Permutation, step 2 (one block): expert segment offsets (exclusive scan of the
+// counts), the compacted list of active experts, and the M-tile work list.
+__global__ __launch_bounds__(1024) void scan_experts_kernel(const int32_t* __restrict__ counts,
+                                                            int E, int32_t* __restrict__ offsets,
+                                                            RouteHeader* __restrict__ hdr,
+                                                            int32_t* __restrict__ active,
+                                                            int2* __restrict__ mtiles) {
+  __shared__ int s_cnt[1024], s_act[1024], s_til[1024];
+  const int e = threadIdx.x;
+  const int c = e < E ? counts[e] : 0;
+  const int a = c > 0 ? 1 : 0;
+  const int tl = (c + kMfmaBM - 1) / kMfmaBM;
+  s_cnt[e] = c;
+  s_act[e] = a;
+  s_til[e] = tl;
+  for (int off = 1; off < 1024; off <<= 1) {
+    __syncthreads();
+    const int pc = e >= off ? s_cnt[e - off] : 0;
+    const int pa = e >= off ? s_act[e - off] : 0;
+    const int pt = e >= off ? s_til[e - off] : 0;
+    __syncthreads();
+    s_cnt[e] += pc;
+    s_act[e] += pa;
+    s_til[e] += pt;
+  }
+  __syncthreads();
+  if (e < E) {
+    offsets[e] = s_cnt[e] - c;
+    if (a) active[s_act[e] - 1] = e;
+    const int t0 = s_til[e] - tl;
+    for (int i = 0; i < tl; ++i) mtiles[t0 + i] = make_int2(e, i * kMfmaBM);
+  }
+  if (e == E - 1) {
+    offsets[E] = s_cnt[e];
+    hdr->n_active = s_act[e];
+    hdr->n_mtiles = s_til[e];
+  }
+}
+
+hipError_t launch_scan(int32_t* chunk_cnt, int nchunks, int E, int32_t* counts, int32_t* offsets,
+                       RouteHeader* hdr, int32_t* active, int2* mtiles, hipStream_t s) {
+  scan_chunks_kernel<<<dim3((E + 3) / 4), 256, 0, s>>>(chunk_cnt, nchunks, E, counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  scan_experts_kernel<<<1, 1024, 0, s>>>(counts, E, offsets, hdr, active, mtiles);
+  return hipGetLastError();
+}
+
+// Permutation, step 3: stable scatter.  One block per chunk, one thread per
+// expert: the assignments of the chunk that chose expert e get consecutive rows
+// of e's segment in (token, j) order.
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ topk_idx,
+                                                      const int32_t* __restrict__ chunk_base,
+                                                      const int32_t* __restrict__ offsets,
+                                                      int64_t T, int E, int k,
+                                                      int32_t* __restrict__ perm_token,
+                                                      int32_t* __restrict__ row_of) {
+  __shared__ int s_idx[kChunkTokens * 16];
+  const int64_t t0 = (int64_t)blockIdx.x * kChunkTokens;
+  const int ntok = (int)min<int64_t>(kChunkTokens, T - t0);
+  for (int i = threadIdx.x; i < ntok * k; i += blockDim.x) s_idx[i] = topk_idx[t0 * k + i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int row = offsets[e] + chunk_base[(int64_t)blockIdx.x * E + e];
+    for (int i = 0; i < ntok * k; ++i) {
+      if (s_idx[i] == e) {
+        perm_token[row] = (int32_t)(t0 + i / k);
+        row_of[t0 * k + i] = row;
+        ++row;
+      }
+    }
+  }
+}
+
+hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* chunk_base,
+                          const int32_t* offsets, int64_t T, int E, int k, int32_t* perm_token,
+                          int32_t* row_of, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int64_t nchunks = (T + kChunkTokens - 1) / kChunkTokens;
+  scatter_kernel<<<dim3((unsigned)nchunks), 256, 0, s>>>(topk_idx, chunk_base, offsets, T, E, k,
+                                                         perm_token, row_of);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Shared expert: act[t][n] = D(silu(g) * u), g and u summed over the split-K
+// partials of the fused [gate | up] product.
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_finalize_kernel(const float* __restrict__ part,
+                                                              int splits, int64_t Tn, int Is,
+                                                              T* __restrict__ act) {
+  const int64_t t = blockIdx.y;
+  const int n4 = blockIdx.x * blockDim.x + threadIdx.x;  // group of 4 columns
+  if (n4 * 4 >= Is) return;
+  float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int z = 0; z < splits; ++z) {
+    const float* p = part + ((int64_t)z * Tn + t) * (2 * (int64_t)Is);
+    const float4 gv = *reinterpret_cast<const float4*>(p + n4 * 4);
+    const float4 uv = *reinterpret_cast<const float4*>(p + Is + n4 * 4);
+    g[0] += gv.x; g[1] += gv.y; g[2] += gv.z; g[3] += gv.w;
+    u[0] += uv.x; u[1] += uv.y; u[2] += uv.z; u[3] += uv.w;
+  }
+  T* o = act + t * Is + n4 * 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float v = silu(g[q]) * u[q];
+    if constexpr (sizeof(T) == 2)
+      reinterpret_cast<uint16_t*>(o)[q] = (uint16_t)f32_to_bf16_bits(v);
+    else
+      reinterpret_cast<float*>(o)[q] = v;
+  }
+}
+
+hipError_t launch_swiglu_finalize(int dtype, const float* part, int splits, int64_t T, int Is,
+                                  void* act, hipStream_t s) {
+  if (T == 0 || Is == 0) return hipSuccess;
+  dim3 grid((Is / 4 + 255) / 256, (unsigned)T);
+  if (dtype == kBF16)
+    swiglu_finalize_kernel<bf16><<<grid, 256, 0, s>>>(part, splits, T, Is, (bf16*)act);
+  else
+    swiglu_finalize_kernel<float><<<grid, 256, 0, s>>>(part, splits, T, Is, (float*)act);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Combine ("GLM-5 · Input features", excerpt block: the residual is the
+// pre-norm input).  out[t] = D(x[t] + (shared[t] + sum_j w[t][j] * y[row_of[t][j]]))
+// in fp32 with j ascending; one 16-byte vector per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* x, const float* __restrict__ sp,
+                                                      int splits, const T* __restrict__ y,
+                                                      const float* __restrict__ w,
+                                                      const int32_t* __restrict__ row_of,
+                                                      int64_t Tn, int d, int k, T* out) {
+  constexpr int V = Elem<T>::kVec;
+  const int64_t t = blockIdx.y;
+  const int c = (blockIdx.x * blockDim.x + threadIdx.x) * V;
+  if (c >= d) return;
+  float acc[V];
+#pragma unroll
+  for (int q = 0; q < V; ++q) acc[q] = 0.f;
+  for (int z = 0; z < splits; ++z) {
+    const float* p = sp + ((int64_t)z * Tn + t) * d + c;
+#pragma unroll
+    for (int q = 0; q < V; q += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(p + q);
+      acc[q] += v.x; acc[q + 1] += v.y; acc[q + 2] += v.z; acc[q + 3] += v.w;
+    }
+  }
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[t * k + j];
+    const int64_t r = row_of[t * k + j];
+    float yv[V];
+    Elem<T>::unpack(ldg16(y + r * d + c), yv);
+#pragma unroll
+    for (int q = 0; q < V; ++q) acc[q] += wj * yv[q];
+  }
+  float xv[V];
+  Elem<T>::unpack(ldg16(x + t * d + c), xv);
+#pragma unroll
+  for (int q = 0; q < V; ++q) xv[q] = xv[q] + acc[q];
+  stg16(out + t * d + c, Elem<T>::pack(xv));
+}
+
+hipError_t launch_combine(int dtype, const void* x, const float* shared_part, int splits,
+                          const void* y, const float* topk_w, const int32_t* row_of, int64_t T,
+                          int d, int k, void* out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int V = dtype == kBF16 ? 8 : 4;
+  dim3 grid((d / V + 255) / 256, (unsigned)T);
+  if (dtype == kBF16)
+    combine_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)x, shared_part, splits,
+                                               (const bf16*)y, topk_w, row_of, T, d, k,
+                                               (bf16*)out);
+  else
+    combine_kernel<float><<<grid, 256, 0, s>>>((const float*)x, shared_part, splits,
+                                                (const float*)y, topk_w, row_of, T, d, k,
+                                                (float*)out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,93 @@
+// Internal launch interface between the host library (moe_api.hip) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum DType { kF32 = 0, kBF16 = 1 };
+
+// Tokens handled by one block of the top-k and scatter kernels (one "chunk").
+constexpr int kChunkTokens = 16;
+// Rows per M-tile of the grouped MFMA kernels.
+constexpr int kMfmaBM = 128;
+// B-columns per N-tile of the MFMA kernels (gate+up halves for SwiGLU).
+constexpr int kMfmaBN = 128;
+constexpr int kMfmaBK = 64;
+// Tile of the fp32 FMA GEMM (router / shared expert of fp32 plans).
+constexpr int kFmaTile = 32;
+
+// Device-side routing summary written by the scan kernel.
+struct RouteHeader {
+  int32_t n_active;  // experts with at least one token
+  int32_t n_mtiles;  // M-tiles of kMfmaBM rows over all experts
+  int32_t pad[14];
+};
+
+// ---------------------------------------------------------------- small kernels
+hipError_t launch_rmsnorm(int dtype, const void* x, const void* w, void* h, int64_t T, int d,
+                          float eps, hipStream_t s);
+
+// out_part[z][m][n] = sum_{k in split z} A[m][k] * B[n][k]; B row n is
+// B1 + n*ldb for n < n_split, else B2 + (n - n_split)*ldb.  fp32 results.
+struct NtArgs {
+  const void* A;
+  int64_t lda;
+  const void* B1;
+  const void* B2;
+  int64_t ldb;
+  int n_split;
+  float* out;  // [splits][M][N]
+  int M, N, K;
+  int splits;
+  int k_tiles_per_split;  // in units of the kernel's K tile
+};
+hipError_t launch_fma_nt(int dtype, const NtArgs& a, hipStream_t s);
+hipError_t launch_mfma_nt(const NtArgs& a, hipStream_t s);
+
+hipError_t launch_topk(const float* logit_part, int splits, const float* corr_bias, int64_t T,
+                       int E, int k, float routed_scale, int32_t* topk_idx, float* topk_w,
+                       int32_t* chunk_cnt, hipStream_t s);
+
+hipError_t launch_scan(int32_t* chunk_cnt, int nchunks, int E, int32_t* counts, int32_t* offsets,
+                       RouteHeader* hdr, int32_t* active, int2* mtiles, hipStream_t s);
+
+hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* chunk_base,
+                          const int32_t* offsets, int64_t T, int E, int k, int32_t* perm_token,
+                          int32_t* row_of, hipStream_t s);
+
+// act[t][n] = D(silu(sum_z P[z][t][n]) * sum_z P[z][t][Is + n])
+hipError_t launch_swiglu_finalize(int dtype, const float* part, int splits, int64_t T, int Is,
+                                  void* act, hipStream_t s);
+
+// out[t] = D(x[t] + (sum_z Ps[z][t] + sum_j w[t][j] * y[row_of[t][j]]))
+hipError_t launch_combine(int dtype, const void* x, const float* shared_part, int splits,
+                          const void* y, const float* topk_w, const int32_t* row_of, int64_t T,
+                          int d, int k, void* out, hipStream_t s);
+
+// ---------------------------------------------------------------- routed experts
+struct GroupArgs {
+  const int32_t* counts;
+  const int32_t* offsets;
+  const RouteHeader* hdr;
+  const int32_t* active;     // compacted active expert ids (stream kernels)
+  const int2* mtiles;        // (expert, first row) per M-tile (MFMA kernels)
+  const int32_t* perm_token; // token of each permuted row (gate_up gathers h rows)
+  int E, d, I;
+};
+
+// act[row][n] = D(silu(h[tok] . G[:, n]) * (h[tok] . G[:, I + n]))  for every permuted row
+hipError_t launch_stream_gate_up(int dtype, const GroupArgs& g, const void* h,
+                                 const void* gate_up, void* act, hipStream_t s);
+// y[row][c] = D(act[row] . down[e][:, c])
+hipError_t launch_stream_down(int dtype, const GroupArgs& g, const void* act, const void* down,
+                              void* y, hipStream_t s);
+
+hipError_t launch_mfma_gate_up(const GroupArgs& g, int max_mtiles, const void* h,
+                               const void* gate_up, void* act, hipStream_t s);
+hipError_t launch_mfma_down(const GroupArgs& g, int max_mtiles, const void* act, const void* down,
+                            void* y, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,448 @@
+// Host side of the C ABI declared in include/moe.h: plan creation and
+// validation, workspace layout, the launch sequence of one forward call, the
+// readers of routing / intermediate buffers, and optional per-stage timing.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "kernels.h"
+#include "moe.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxExperts = 1024;
+// Decode-sized batches (mean tokens per routed expert at most this) take the
+// weight-streaming kernels under MOE_PATH_AUTO.
+constexpr int kStreamMaxMeanTokens = 8;
+// Split-K target: enough blocks for two per compute unit on 256 CUs.
+constexpr int kTargetBlocks = 512;
+
+enum Stage {
+  kStNorm = 0,
+  kStRouter,
+  kStTopk,
+  kStScan,
+  kStScatter,
+  kStGateUp,
+  kStSharedGateUp,
+  kStSharedAct,
+  kStDown,
+  kStSharedDown,
+  kStCombine,
+  kNumStages
+};
+const char* const kStageNames[kNumStages] = {
+    "rmsnorm",       "router_logits",   "router_topk", "permute_scan", "permute_scatter",
+    "expert_gate_up", "shared_gate_up", "shared_act",  "expert_down",  "shared_down",
+    "combine"};
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Split {
+  int splits;
+  int kt_per;
+};
+
+// Split-K factor for a dense K-contiguous product of M rows, N columns, K depth.
+Split nt_split(int64_t M, int64_t N, int64_t K, int tm, int tn, int tk) {
+  const int64_t tiles = cdiv(M, tm) * cdiv(N, tn);
+  const int64_t nkt = K / tk;
+  int64_t s = std::max<int64_t>(1, cdiv(kTargetBlocks, std::max<int64_t>(tiles, 1)));
+  s = std::min<int64_t>(s, std::max<int64_t>(1, nkt / 2));
+  const int64_t per = cdiv(nkt, s);
+  return Split{(int)cdiv(nkt, per), (int)per};
+}
+
+struct Layout {
+  size_t h, logits, topk_idx, topk_w, chunk_cnt, counts, offsets, hdr, active, mtiles,
+      perm_token, row_of, act, y, sh_gu, act_s, sh_dn, total;
+};
+
+struct EventPair {
+  int stage;
+  hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct moe_plan {
+  moe_config_t cfg;
+  size_t es;  // bytes per element of D
+  Layout lay;
+  // stage timing (the only mutable state of a plan)
+  std::mutex tmu;
+  bool timing = false;
+  std::vector<EventPair> pending;
+  std::vector<hipEvent_t> pool;
+};
+
+namespace {
+
+bool use_mfma(const moe_plan* p, int64_t T, int k) {
+  if (p->cfg.dtype != MOE_DTYPE_BF16) return false;
+  if (p->cfg.path == MOE_PATH_STREAM) return false;
+  if (p->cfg.path == MOE_PATH_MFMA) return true;
+  return T * k > (int64_t)kStreamMaxMeanTokens * p->cfg.n_experts;
+}
+
+// Tile sizes of the dense K-contiguous products for this plan's dtype.
+void nt_tiles(const moe_plan* p, int* tm, int* tn, int* tk) {
+  if (p->cfg.dtype == MOE_DTYPE_BF16) {
+    *tm = kMfmaBM;
+    *tn = kMfmaBN;
+    *tk = kMfmaBK;
+  } else {
+    *tm = *tn = *tk = kFmaTile;
+  }
+}
+
+// Largest split-K partial buffer (in fp32 elements) over every T <= Tmax.
+size_t max_partial_elems(const moe_plan* p, int64_t Tmax, int64_t N, int64_t K) {
+  int tm, tn, tk;
+  nt_tiles(p, &tm, &tn, &tk);
+  size_t best = 0;
+  for (int64_t m = 1; m <= std::max<int64_t>(1, cdiv(Tmax, tm)); ++m) {
+    const int64_t T = std::min<int64_t>(m * tm, std::max<int64_t>(Tmax, 1));
+    const Split s = nt_split(T, N, K, tm, tn, tk);
+    best = std::max(best, (size_t)s.splits * (size_t)T * (size_t)N);
+  }
+  return best;
+}
+
+void make_layout(moe_plan* p) {
+  const moe_config_t& c = p->cfg;
+  const int64_t T = std::max<int64_t>(c.max_tokens, 1);
+  const int64_t A = T * c.max_top_k;
+  const int64_t nch = cdiv(T, kChunkTokens);
+  const size_t es = p->es;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(std::max<size_t>(bytes, 1));
+    return at;
+  };
+  Layout& L = p->lay;
+  L.h = take((size_t)T * c.dim * es);
+  L.logits = take(max_partial_elems(p, T, c.n_experts, c.dim) * 4);
+  L.topk_idx = take((size_t)A * 4);
+  L.topk_w = take((size_t)A * 4);
+  L.chunk_cnt = take((size_t)nch * c.n_experts * 4);
+  L.counts = take((size_t)c.n_experts * 4);
+  L.offsets = take((size_t)(c.n_experts + 1) * 4);
+  L.hdr = take(sizeof(RouteHeader));
+  L.active = take((size_t)c.n_experts * 4);
+  L.mtiles = take((size_t)(cdiv(A, kMfmaBM) + std::min<int64_t>(c.n_experts, A)) * sizeof(int2));
+  L.perm_token = take((size_t)A * 4);
+  L.row_of = take((size_t)A * 4);
+  L.act = take((size_t)A * c.moe_inter * es);
+  L.y = take((size_t)A * c.dim * es);
+  if (c.shared_inter > 0) {
+    L.sh_gu = take(max_partial_elems(p, T, 2 * (int64_t)c.shared_inter, c.dim) * 4);
+    L.act_s = take((size_t)T * c.shared_inter * es);
+    L.sh_dn = take(max_partial_elems(p, T, c.dim, c.shared_inter) * 4);
+  } else {
+    L.sh_gu = L.act_s = L.sh_dn = 0;
+  }
+  L.total = off;
+}
+
+bool misaligned(const void* ptr) { return ((uintptr_t)ptr & 15u) != 0; }
+
+hipEvent_t get_event(moe_plan* p) {
+  if (!p->pool.empty()) {
+    hipEvent_t e = p->pool.back();
+    p->pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_SUCCESS: return "success";
+    case MOE_ERROR_INVALID_VALUE: return "invalid value";
+    case MOE_ERROR_NOT_SUPPORTED: return "not supported";
+    case MOE_ERROR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERROR_MISALIGNED: return "pointer not 16-byte aligned";
+    case MOE_ERROR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* moe_stage_name(int32_t stage) {
+  if (stage < 0 || stage >= kNumStages) return nullptr;
+  return kStageNames[stage];
+}
+
+moe_status_t moe_plan_create(const moe_config_t* cfg, moe_plan_t* plan, size_t* workspace_bytes) {
+  if (!cfg || !plan || !workspace_bytes) return MOE_ERROR_INVALID_VALUE;
+  *plan = nullptr;
+  if (cfg->struct_size != sizeof(moe_config_t)) return MOE_ERROR_INVALID_VALUE;
+  if (cfg->dim <= 0 || cfg->n_experts <= 0 || cfg->moe_inter <= 0 || cfg->shared_inter < 0 ||
+      cfg->max_tokens < 0 || cfg->max_top_k < 1 || cfg->max_top_k > cfg->n_experts ||
+      !(cfg->eps > 0.0f) || !isfinite(cfg->eps) || cfg->flags != 0)
+    return MOE_ERROR_INVALID_VALUE;
+  if (cfg->dtype != MOE_DTYPE_F32 && cfg->dtype != MOE_DTYPE_BF16) return MOE_ERROR_NOT_SUPPORTED;
+  if (cfg->path < MOE_PATH_AUTO || cfg->path > MOE_PATH_MFMA) return MOE_ERROR_INVALID_VALUE;
+  if (cfg->path == MOE_PATH_MFMA && cfg->dtype != MOE_DTYPE_BF16) return MOE_ERROR_NOT_SUPPORTED;
+  if (cfg->dim % 64 || cfg->moe_inter % 64 || cfg->shared_inter % 64 ||
+      cfg->n_experts > kMaxExperts || cfg->max_top_k > kMaxTopK)
+    return MOE_ERROR_NOT_SUPPORTED;
+  // 32-bit row indices inside the kernels
+  if (cfg->max_tokens > (int64_t)1 << 26 || (int64_t)cfg->max_tokens * cfg->max_top_k >= INT32_MAX)
+    return MOE_ERROR_NOT_SUPPORTED;
+  moe_plan* p = new (std::nothrow) moe_plan();
+  if (!p) return MOE_ERROR_INVALID_VALUE;
+  p->cfg = *cfg;
+  p->es = cfg->dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  make_layout(p);
+  *plan = p;
+  *workspace_bytes = p->lay.total;
+  return MOE_SUCCESS;
+}
+
+moe_status_t moe_plan_destroy(moe_plan_t p) {
+  if (!p) return MOE_SUCCESS;
+  for (auto& ev : p->pending) {
+    (void)hipEventDestroy(ev.a);
+    (void)hipEventDestroy(ev.b);
+  }
+  for (auto e : p->pool) (void)hipEventDestroy(e);
+  delete p;
+  return MOE_SUCCESS;
+}
+
+int32_t moe_plan_path(moe_plan_t p, int64_t num_tokens, int32_t top_k) {
+  if (!p) return -1;
+  return use_mfma(p, num_tokens, top_k) ? MOE_PATH_MFMA : MOE_PATH_STREAM;
+}
+
+moe_status_t moe_set_stage_timing(moe_plan_t p, int32_t enable) {
+  if (!p) return MOE_ERROR_INVALID_VALUE;
+  std::lock_guard<std::mutex> g(p->tmu);
+  p->timing = enable != 0;
+  return MOE_SUCCESS;
+}
+
+moe_status_t moe_stage_times(moe_plan_t p, double* ms, int64_t* calls) {
+  if (!p || !ms) return MOE_ERROR_INVALID_VALUE;
+  std::lock_guard<std::mutex> g(p->tmu);
+  for (int i = 0; i < MOE_MAX_STAGES; ++i) ms[i] = 0.0;
+  int64_t n_norm = 0;
+  for (auto& ev : p->pending) {
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, ev.a, ev.b) != hipSuccess) return MOE_ERROR_HIP;
+    ms[ev.stage] += t;
+    if (ev.stage == kStNorm) ++n_norm;
+    p->pool.push_back(ev.a);
+    p->pool.push_back(ev.b);
+  }
+  p->pending.clear();
+  if (calls) *calls = n_norm;
+  return MOE_SUCCESS;
+}
+
+moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_bytes,
+                               void* stream, int64_t T, const void* x, const void* norm_w,
+                               const void* router_w, const float* corr_bias, const void* gate_up,
+                               const void* down, const void* shared_gate, const void* shared_up,
+                               const void* shared_down, int32_t k, float routed_scale,
+                               void* out) {
+  if (!p) return MOE_ERROR_INVALID_VALUE;
+  const moe_config_t& c = p->cfg;
+  if (T < 0 || T > c.max_tokens) return MOE_ERROR_INVALID_VALUE;
+  if (k < 1 || k > c.max_top_k || k > c.n_experts) return MOE_ERROR_INVALID_VALUE;
+  if (!isfinite(routed_scale)) return MOE_ERROR_INVALID_VALUE;
+  if (!workspace || !x || !norm_w || !router_w || !corr_bias || !gate_up || !down || !out)
+    return MOE_ERROR_INVALID_VALUE;
+  const bool has_shared = c.shared_inter > 0;
+  if (has_shared && (!shared_gate || !shared_up || !shared_down)) return MOE_ERROR_INVALID_VALUE;
+  if (misaligned(workspace) || misaligned(x) || misaligned(norm_w) || misaligned(router_w) ||
+      misaligned(corr_bias) || misaligned(gate_up) || misaligned(down) || misaligned(out) ||
+      (has_shared && (misaligned(shared_gate) || misaligned(shared_up) || misaligned(shared_down))))
+    return MOE_ERROR_MISALIGNED;
+  if (workspace_bytes < p->lay.total) return MOE_ERROR_WORKSPACE_TOO_SMALL;
+  if (T == 0) return MOE_SUCCESS;
+
+  hipStream_t s = (hipStream_t)stream;
+  const Layout& L = p->lay;
+  char* ws = (char*)workspace;
+  void* h = ws + L.h;
+  float* logits = (float*)(ws + L.logits);
+  int32_t* topk_idx = (int32_t*)(ws + L.topk_idx);
+  float* topk_w = (float*)(ws + L.topk_w);
+  int32_t* chunk_cnt = (int32_t*)(ws + L.chunk_cnt);
+  int32_t* counts = (int32_t*)(ws + L.counts);
+  int32_t* offsets = (int32_t*)(ws + L.offsets);
+  RouteHeader* hdr = (RouteHeader*)(ws + L.hdr);
+  int32_t* active = (int32_t*)(ws + L.active);
+  int2* mtiles = (int2*)(ws + L.mtiles);
+  int32_t* perm_token = (int32_t*)(ws + L.perm_token);
+  int32_t* row_of = (int32_t*)(ws + L.row_of);
+  void* act = ws + L.act;
+  void* y = ws + L.y;
+  float* sh_gu = (float*)(ws + L.sh_gu);
+  void* act_s = ws + L.act_s;
+  float* sh_dn = (float*)(ws + L.sh_dn);
+
+  const int dt = c.dtype == MOE_DTYPE_BF16 ? kBF16 : kF32;
+  const int E = c.n_experts, d = c.dim, I = c.moe_inter, Is = c.shared_inter;
+  const int64_t A = T * k;
+  const int nchunks = (int)cdiv(T, kChunkTokens);
+  const bool mfma = use_mfma(p, T, k);
+  int tm, tn, tk;
+  nt_tiles(p, &tm, &tn, &tk);
+
+  std::unique_lock<std::mutex> tlock(p->tmu, std::defer_lock);
+  bool timing = false;
+  {
+    std::lock_guard<std::mutex> g(p->tmu);
+    timing = p->timing;
+  }
+  if (timing) tlock.lock();
+  hipError_t err = hipSuccess;
+  auto stage = [&](int st, auto&& fn) {
+    if (err != hipSuccess) return;
+    EventPair ev{st, nullptr, nullptr};
+    if (timing) {
+      ev.a = get_event(p);
+      ev.b = get_event(p);
+      if (!ev.a || !ev.b) {
+        err = hipErrorOutOfMemory;
+        return;
+      }
+      err = hipEventRecord(ev.a, s);
+      if (err != hipSuccess) return;
+    }
+    err = fn();
+    if (timing) {
+      const hipError_t e2 = hipEventRecord(ev.b, s);
+      if (err == hipSuccess) err = e2;
+      p->pending.push_back(ev);
+    }
+  };
+  auto nt = [&](const void* Aop, int64_t lda, const void* B1, const void* B2, int64_t ldb,
+                int n_split, float* outp, int64_t N, int64_t K) {
+    const Split sp = nt_split(T, N, K, tm, tn, tk);
+    NtArgs a{Aop, lda, B1, B2, ldb, n_split, outp, (int)T, (int)N, (int)K, sp.splits, sp.kt_per};
+    return dt == kBF16 ? launch_mfma_nt(a, s) : launch_fma_nt(dt, a, s);
+  };
+  const Split rsplit = nt_split(T, E, d, tm, tn, tk);
+  const Split sdsplit = has_shared ? nt_split(T, d, Is, tm, tn, tk) : Split{0, 0};
+  const Split sgsplit = has_shared ? nt_split(T, 2 * (int64_t)Is, d, tm, tn, tk) : Split{0, 0};
+
+  stage(kStNorm, [&] { return launch_rmsnorm(dt, x, norm_w, h, T, d, c.eps, s); });
+  stage(kStRouter, [&] { return nt(h, d, router_w, router_w, d, E, logits, E, d); });
+  stage(kStTopk, [&] {
+    return launch_topk(logits, rsplit.splits, corr_bias, T, E, k, routed_scale, topk_idx, topk_w,
+                       chunk_cnt, s);
+  });
+  stage(kStScan, [&] {
+    return launch_scan(chunk_cnt, nchunks, E, counts, offsets, hdr, active, mtiles, s);
+  });
+  stage(kStScatter, [&] {
+    return launch_scatter(topk_idx, chunk_cnt, offsets, T, E, k, perm_token, row_of, s);
+  });
+  GroupArgs g{counts, offsets, hdr, active, mtiles, perm_token, E, d, I};
+  const int max_mtiles = (int)(cdiv(A, kMfmaBM) + std::min<int64_t>(E, A));
+  stage(kStGateUp, [&] {
+    return mfma ? launch_mfma_gate_up(g, max_mtiles, h, gate_up, act, s)
+                : launch_stream_gate_up(dt, g, h, gate_up, act, s);
+  });
+  if (has_shared) {
+    stage(kStSharedGateUp,
+          [&] { return nt(h, d, shared_gate, shared_up, d, Is, sh_gu, 2 * (int64_t)Is, d); });
+    stage(kStSharedAct,
+          [&] { return launch_swiglu_finalize(dt, sh_gu, sgsplit.splits, T, Is, act_s, s); });
+  }
+  stage(kStDown, [&] {
+    return mfma ? launch_mfma_down(g, max_mtiles, act, down, y, s)
+                : launch_stream_down(dt, g, act, down, y, s);
+  });
+  if (has_shared)
+    stage(kStSharedDown, [&] { return nt(act_s, Is, shared_down, shared_down, Is, d, sh_dn, d, Is); });
+  stage(kStCombine, [&] {
+    return launch_combine(dt, x, sh_dn, has_shared ? sdsplit.splits : 0, y, topk_w, row_of, T, d,
+                          k, out, s);
+  });
+  return err == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
+}
+
+size_t moe_buffer_bytes(moe_plan_t p, int64_t T, int32_t k, int32_t which) {
+  if (!p || T < 0 || T > p->cfg.max_tokens || k < 1 || k > p->cfg.max_top_k) return 0;
+  const moe_config_t& c = p->cfg;
+  const int64_t A = T * k;
+  switch (which) {
+    case MOE_BUF_H: return (size_t)T * c.dim * p->es;
+    case MOE_BUF_OFFSETS: return (size_t)(c.n_experts + 1) * 4;
+    case MOE_BUF_PERM_TOKEN: return (size_t)A * 4;
+    case MOE_BUF_ROW_OF: return (size_t)A * 4;
+    case MOE_BUF_ACT: return (size_t)A * c.moe_inter * p->es;
+    case MOE_BUF_Y: return (size_t)A * c.dim * p->es;
+    case MOE_BUF_SHARED_ACT: return (size_t)T * c.shared_inter * p->es;
+  }
+  return 0;
+}
+
+moe_status_t moe_read_buffer(moe_plan_t p, const void* workspace, void* stream, int64_t T,
+                             int32_t k, int32_t which, void* dst, size_t dst_bytes) {
+  if (!p || !workspace || !dst) return MOE_ERROR_INVALID_VALUE;
+  if (which < 0 || which >= MOE_BUF_COUNT) return MOE_ERROR_INVALID_VALUE;
+  if (T < 0 || T > p->cfg.max_tokens || k < 1 || k > p->cfg.max_top_k) return MOE_ERROR_INVALID_VALUE;
+  const size_t bytes = moe_buffer_bytes(p, T, k, which);
+  if (dst_bytes < bytes) return MOE_ERROR_INVALID_VALUE;
+  if (bytes == 0) return MOE_SUCCESS;
+  const Layout& L = p->lay;
+  size_t off = 0;
+  switch (which) {
+    case MOE_BUF_H: off = L.h; break;
+    case MOE_BUF_OFFSETS: off = L.offsets; break;
+    case MOE_BUF_PERM_TOKEN: off = L.perm_token; break;
+    case MOE_BUF_ROW_OF: off = L.row_of; break;
+    case MOE_BUF_ACT: off = L.act; break;
+    case MOE_BUF_Y: off = L.y; break;
+    case MOE_BUF_SHARED_ACT: off = L.act_s; break;
+  }
+  const hipError_t e = hipMemcpyAsync(dst, (const char*)workspace + off, bytes,
+                                      hipMemcpyDeviceToDevice, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
+}
+
+moe_status_t moe_read_routing(moe_plan_t p, const void* workspace, void* stream, int64_t T,
+                              int32_t k, int32_t* topk_idx, float* topk_w, int32_t* counts) {
+  if (!p || !workspace) return MOE_ERROR_INVALID_VALUE;
+  if (T < 0 || T > p->cfg.max_tokens || k < 1 || k > p->cfg.max_top_k) return MOE_ERROR_INVALID_VALUE;
+  const Layout& L = p->lay;
+  const char* ws = (const char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t ab = (size_t)T * k * 4;
+  hipError_t e = hipSuccess;
+  if (topk_idx && ab) e = hipMemcpyAsync(topk_idx, ws + L.topk_idx, ab, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess && topk_w && ab)
+    e = hipMemcpyAsync(topk_w, ws + L.topk_w, ab, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess && counts)
+    e = hipMemcpyAsync(counts, ws + L.counts, (size_t)p->cfg.n_experts * 4,
+                       hipMemcpyDeviceToDevice, s);
+  return e == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
+}
+
+}  // extern "C"

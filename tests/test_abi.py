@@ -1,0 +1,143 @@
+"""The C-ABI library loads, exports every symbol include/moe.h declares, and
+validates its arguments on the host (no device work is enqueued by any call
+made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_transformer_rmsnorm_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return sorted(set(re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", src)))
+
+
+def test_header_declarations_are_exported():
+    names = _declared()
+    assert "moe_block_forward" in names and "moe_plan_create" in names
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(moe.EXPORTS) == names
+
+
+def test_abi_version_and_strings():
+    assert moe.moe_abi_version() == moe.ABI_VERSION
+    assert moe.moe_status_string(moe.MOE_ERROR_WORKSPACE_TOO_SMALL) == "workspace too small"
+    assert moe.moe_stage_name(0) == "rmsnorm" and moe.moe_stage_name(99) is None
+    assert ctypes.sizeof(moe.moe_config_t) == 48
+
+
+def _cfg(**kw):
+    base = dict(dim=6144, max_tokens=64, n_experts=256, moe_inter=2048, shared_inter=2048,
+                max_top_k=8, dtype="bf16")
+    base.update(kw)
+    return moe.make_config(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dim=100), moe.MOE_ERROR_NOT_SUPPORTED),
+    (dict(moe_inter=96), moe.MOE_ERROR_NOT_SUPPORTED),
+    (dict(shared_inter=32), moe.MOE_ERROR_NOT_SUPPORTED),
+    (dict(max_top_k=17, n_experts=32), moe.MOE_ERROR_NOT_SUPPORTED),
+    (dict(n_experts=2048), moe.MOE_ERROR_NOT_SUPPORTED),
+    (dict(max_top_k=0), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(max_top_k=9, n_experts=8), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(max_tokens=-1), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(eps=0.0), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(dtype=7), moe.MOE_ERROR_NOT_SUPPORTED),
+    (dict(dtype="f32", path=moe.MOE_PATH_MFMA), moe.MOE_ERROR_NOT_SUPPORTED),
+    (dict(path=5), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(flags=1), moe.MOE_ERROR_INVALID_VALUE),
+])
+def test_plan_validation(kw, status):
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_plan_create(_cfg(**kw))
+    assert ei.value.status == status
+
+
+def test_plan_struct_size_checked():
+    cfg = _cfg()
+    cfg.struct_size = 40
+    with pytest.raises(moe.MoEError):
+        moe.moe_plan_create(cfg)
+
+
+def test_workspace_sizing_and_path_choice():
+    plan, ws = moe.moe_plan_create(_cfg(max_tokens=16384))
+    try:
+        assert moe.moe_plan_path(plan, 64, 8) == moe.MOE_PATH_STREAM     # decode: stream weights
+        assert moe.moe_plan_path(plan, 4096, 8) == moe.MOE_PATH_MFMA     # prefill: matrix cores
+        A = 16384 * 8
+        # act [A, I] + y [A, d] in bf16 dominate the workspace
+        assert ws >= 2 * A * (2048 + 6144)
+        assert moe.moe_buffer_bytes(plan, 100, 8, moe.MOE_BUF_Y) == 100 * 8 * 6144 * 2
+        assert moe.moe_buffer_bytes(plan, 100, 9, moe.MOE_BUF_Y) == 0
+    finally:
+        moe.moe_plan_destroy(plan)
+    plan, ws32 = moe.moe_plan_create(_cfg(dtype="f32", dim=256, n_experts=8, moe_inter=128,
+                                          shared_inter=0, max_top_k=2))
+    assert moe.moe_plan_path(plan, 64, 2) == moe.MOE_PATH_STREAM
+    moe.moe_plan_destroy(plan)
+
+
+FAKE = 1 << 20  # aligned, never dereferenced: every call below fails validation
+
+
+def _fwd(plan, ws, **kw):
+    args = dict(plan=plan, workspace=FAKE, workspace_bytes=ws, stream=0, num_tokens=8, x=FAKE,
+                norm_w=FAKE, router_w=FAKE, corr_bias=FAKE, gate_up=FAKE, down=FAKE,
+                shared_gate=FAKE, shared_up=FAKE, shared_down=FAKE, top_k=8, routed_scale=2.5,
+                out=FAKE)
+    args.update(kw)
+    moe.moe_block_forward(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_tokens=65), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(num_tokens=-1), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(top_k=0), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(top_k=9), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(routed_scale=float("inf")), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(routed_scale=float("nan")), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(x=None), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(shared_down=None), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(workspace=None), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(gate_up=FAKE + 8), moe.MOE_ERROR_MISALIGNED),
+    (dict(out=FAKE + 2), moe.MOE_ERROR_MISALIGNED),
+    (dict(workspace_bytes=1024), moe.MOE_ERROR_WORKSPACE_TOO_SMALL),
+])
+def test_forward_validation(kw, status):
+    plan, ws = moe.moe_plan_create(_cfg())
+    try:
+        with pytest.raises(moe.MoEError) as ei:
+            _fwd(plan, ws, **kw)
+        assert ei.value.status == status
+    finally:
+        moe.moe_plan_destroy(plan)
+
+
+def test_zero_tokens_succeeds_without_device_work():
+    plan, ws = moe.moe_plan_create(_cfg())
+    try:
+        _fwd(plan, ws, num_tokens=0)
+    finally:
+        moe.moe_plan_destroy(plan)
+
+
+def test_reader_validation():
+    plan, ws = moe.moe_plan_create(_cfg())
+    try:
+        with pytest.raises(moe.MoEError):
+            moe.moe_read_buffer(plan, FAKE, 0, 8, 8, 99, FAKE, 1 << 30)
+        with pytest.raises(moe.MoEError):
+            moe.moe_read_buffer(plan, FAKE, 0, 8, 8, moe.MOE_BUF_Y, FAKE, 16)
+        with pytest.raises(moe.MoEError):
+            moe.moe_read_routing(plan, FAKE, 0, 65, 8)
+    finally:
+        moe.moe_plan_destroy(plan)
