@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE feed-forward sublayer on one MI355X.
+
+One step = one moe_block_forward over one batch (RMSNorm, router top-k,
+permutation, routed + shared SwiGLU experts, combine + residual) with every
+input resident in HBM.  The headline line is the GLM-5-shaped decode batch
+(64 tokens, d 6144, 256 experts of width 2048, top-8, one shared expert, bf16);
+the same line carries the GLM-5 prefill batch (4096 tokens) as a secondary
+measurement.  Inputs are seeded synthetic tensors (weights N(0, 0.02), x N(0,1),
+gain 1 + N(0, 0.1), correction bias U(-0.01, 0.01)).
+
+Output: one JSON line on stdout.  Progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-block tokens/s at GLM-5 shape (T=64 decode, T=4096 prefill); % roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+DOMINANT = "expert_gate_up"    # the gate_and_up grouped kernel: 2/3 of bytes and FLOPs
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(cfg, counts):
+    """Algorithmic HBM bytes and FLOPs of one step and of one gate_up launch."""
+    b = 2 if cfg.dtype == "bf16" else 4
+    n_active = int((counts > 0).sum())
+    A = cfg.T * cfg.k
+    step_bytes = (n_active * 3 * cfg.d * cfg.I * b + 3 * cfg.d * cfg.Is * b + cfg.E * cfg.d * b
+                  + 4 * cfg.E + cfg.d * b + 2 * cfg.T * cfg.d * b)
+    step_flops = 2 * cfg.T * cfg.E * cfg.d + 6 * A * cfg.d * cfg.I + 6 * cfg.T * cfg.d * cfg.Is
+    # gate_up kernel: per active expert its [d, 2I] weights; plus h rows in, act rows out
+    gu_unit_bytes = cfg.d * 2 * cfg.I * b
+    gu_bytes = n_active * gu_unit_bytes + cfg.T * cfg.d * b + A * cfg.I * b
+    gu_flops = 4 * A * cfg.d * cfg.I
+    return dict(n_active=n_active, step_bytes=step_bytes, step_flops=step_flops,
+                gu_unit_bytes=gu_unit_bytes, gu_bytes=gu_bytes, gu_flops=gu_flops)
+
+
+def run_workload(cfg, tin, steps, warmup):
+    import torch
+    import mixture_experts_transformer_rmsnorm_amd as moe
+
+    weights = {k: tin[k] for k in ("norm_w", "router_w", "corr_bias", "gate_up", "down",
+                                   "shared_gate", "shared_up", "shared_down")}
+    block = moe.MoEBlock(weights, max_tokens=cfg.T, top_k=cfg.k, routed_scale=cfg.routed_scale,
+                         eps=cfg.eps)
+    x = tin["x"]
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        block.forward(x, out=out)
+    torch.cuda.synchronize()
+    _, _, cnt = block.routing(cfg.T)
+    counts = cnt.cpu().numpy()
+    path = moe.moe_plan_path(block.plan, cfg.T, cfg.k)
+
+    # timed region: K steps; HIP events on the forward's stream around the dominant kernel
+    moe.moe_set_stage_timing(block.plan, moe.stage_mask(DOMINANT))
+    moe.moe_stage_times(block.plan)  # reset
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        block.forward(x, out=out, stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stage_ms, calls = moe.moe_stage_times(block.plan)
+    moe.moe_set_stage_timing(block.plan, 0)
+
+    # one more pass with every stage timed, for the per-stage breakdown (not the headline)
+    moe.moe_set_stage_timing(block.plan, moe.stage_mask())
+    for _ in range(min(steps, 10)):
+        block.forward(x, out=out, stream=stream)
+    torch.cuda.synchronize()
+    all_ms, all_calls = moe.moe_stage_times(block.plan)
+    moe.moe_set_stage_timing(block.plan, 0)
+    block.close()
+
+    elapsed = t1 - t0
+    ms_step = 1e3 * elapsed / steps
+    alg = algorithmic(cfg, counts)
+    gu_ms = stage_ms[DOMINANT] / max(calls, 1)
+    gu_s = gu_ms * 1e-3
+    hbm_t = alg["gu_bytes"] / (HBM_PEAK_GBS * 1e9)
+    mfma_t = alg["gu_flops"] / (BF16_PEAK_TFLOPS * 1e12)
+    if hbm_t >= mfma_t:
+        achieved = alg["gu_bytes"] / gu_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = alg["gu_flops"] / gu_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    roof.update(kernel=DOMINANT, kernel_ms=round(gu_ms, 4), algorithmic_bytes=alg["gu_bytes"],
+                algorithmic_flops=alg["gu_flops"], active_experts=alg["n_active"])
+    step_s = ms_step * 1e-3
+    hbm_frac = alg["step_bytes"] / step_s / (HBM_PEAK_GBS * 1e9)
+    mfma_frac = alg["step_flops"] / step_s / (BF16_PEAK_TFLOPS * 1e12)
+    t_roof = max(alg["step_bytes"] / (HBM_PEAK_GBS * 1e9), alg["step_flops"] / (BF16_PEAK_TFLOPS * 1e12))
+    step_roof = {"bytes_alg": alg["step_bytes"], "flops_alg": alg["step_flops"],
+                 "GB_per_s": round(alg["step_bytes"] / step_s / 1e9, 1),
+                 "TFLOP_per_s": round(alg["step_flops"] / step_s / 1e12, 1),
+                 "hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
+                 "frac": round(t_roof / step_s, 4)}
+    per_stage = {k: round(v / max(all_calls, 1), 4) for k, v in all_ms.items() if v > 0}
+    return dict(value=cfg.T * steps / elapsed, ms_per_step=ms_step, roofline=roof,
+                step_roofline=step_roof, stage_ms=per_stage, path=path,
+                max_load=int(counts.max()), counts=counts)
+
+
+def cpu_baseline(cfg, tin, small, seconds):
+    """The CPU oracle, as it stands, on the first tokens of the same batch, in chunks
+    of 8 tokens until about `seconds` of oracle time (full forward: norm, router,
+    selected experts, shared expert, combine)."""
+    import numpy as np
+    import oracle
+    import workloads
+
+    dt = oracle.DTYPES[cfg.dtype]
+    host_gu, host_dn = {}, {}
+    shared = [workloads.torch_to_host(tin[n]) for n in ("shared_gate", "shared_up", "shared_down")]
+    spent, done = 0.0, 0
+    chunk = 8
+    while done < cfg.T and (spent < seconds or done == 0):
+        rows = np.arange(done, min(cfg.T, done + chunk))
+        xs = small["x"][rows]
+        # routing of the chunk decides which expert weights the oracle needs on the host
+        pre = oracle.route(xs, small["norm_w"], small["router_w"], small["corr_bias"], cfg.k,
+                           cfg.routed_scale, dt, cfg.eps)
+        for e in np.unique(pre["idx"]):
+            if e not in host_gu:
+                host_gu[e] = workloads.torch_to_host(tin["gate_up"][e])
+                host_dn[e] = workloads.torch_to_host(tin["down"][e])
+        gu = [host_gu.get(e) for e in range(cfg.E)]
+        dn = [host_dn.get(e) for e in range(cfg.E)]
+        t0 = time.perf_counter()
+        r = oracle.route(xs, small["norm_w"], small["router_w"], small["corr_bias"], cfg.k,
+                         cfg.routed_scale, dt, cfg.eps)
+        oracle.experts(np.arange(len(rows)), xs, r["h"], r["idx"], r["w"], gu, dn, shared[0],
+                       shared[1], shared[2], dt)
+        spent += time.perf_counter() - t0
+        done += len(rows)
+        log("cpu oracle: %d tokens in %.1f s" % (done, spent))
+    return {"value": round(done / spent, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "first %d of the %d %s tokens, full forward (norm, router, %d experts "
+                      "+ shared, combine), %.1f s" % (done, cfg.T, cfg.name, cfg.k, spent)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="glm5_decode")
+    ap.add_argument("--secondary", default="glm5_prefill",
+                    help="second workload of the same shape family reported in the line ('' = none)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+
+    torch.cuda.set_device(0)
+    cfg = workloads.config(args.config)
+    log("drawing %s inputs on the device" % cfg.name)
+    tin = workloads.make_torch(cfg, 0, device="cuda", weights="device")
+    small = workloads.draw_small(cfg, 0)
+    torch.cuda.synchronize()
+    log("timing %s: %d warmup + %d steps" % (cfg.name, args.warmup, args.steps))
+    res = run_workload(cfg, tin, args.steps, args.warmup)
+    log("%s: %.1f tokens/s, %.3f ms/step, gate_up %.3f ms (%s %.1f%%), path %d" % (
+        cfg.name, res["value"], res["ms_per_step"], res["roofline"]["kernel_ms"],
+        res["roofline"]["bound"], 100 * res["roofline"]["frac"], res["path"]))
+    line = {
+        "metric": METRIC, "value": round(res["value"], 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded; random-init weights of the GLM-5 MoE-block shapes)",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "dim": cfg.d, "n_experts": cfg.E,
+                   "moe_inter": cfg.I, "shared_inter": cfg.Is, "top_k": cfg.k,
+                   "routed_scale": cfg.routed_scale, "active_experts": res["roofline"]["active_experts"],
+                   "max_expert_load": res["max_load"],
+                   "kernel_path": "stream" if res["path"] == 1 else "mfma"},
+        "roofline": res["roofline"],
+        "step_roofline": res["step_roofline"],
+        "stage_ms": res["stage_ms"],
+    }
+    if args.secondary:
+        cfg2 = workloads.config(args.secondary)
+        if (cfg2.d, cfg2.E, cfg2.I, cfg2.Is, cfg2.dtype) == (cfg.d, cfg.E, cfg.I, cfg.Is, cfg.dtype):
+            tin2 = dict(tin)
+            small2 = workloads.draw_small(cfg2, 0)
+            for key in ("x", "norm_w", "router_w"):
+                tin2[key] = workloads.host_to_torch(small2[key], cfg2.dtype, "cuda")
+            tin2["corr_bias"] = torch.from_numpy(small2["corr_bias"]).cuda()
+            log("timing %s" % cfg2.name)
+            r2 = run_workload(cfg2, tin2, max(args.steps // 2, 5), args.warmup)
+            log("%s: %.1f tokens/s, %.3f ms/step, gate_up %.3f ms (%s %.1f%%)" % (
+                cfg2.name, r2["value"], r2["ms_per_step"], r2["roofline"]["kernel_ms"],
+                r2["roofline"]["bound"], 100 * r2["roofline"]["frac"]))
+            line["secondary"] = {"workload": cfg2.name, "tokens": cfg2.T,
+                                 "value": round(r2["value"], 1), "unit": "tokens/s",
+                                 "ms_per_step": round(r2["ms_per_step"], 4),
+                                 "kernel_path": "stream" if r2["path"] == 1 else "mfma",
+                                 "roofline": r2["roofline"], "step_roofline": r2["step_roofline"],
+                                 "stage_ms": r2["stage_ms"]}
+            del tin2
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(cfg, tin, small, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

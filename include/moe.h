@@ -117,9 +117,10 @@ MOE_API moe_status_t moe_plan_create(const moe_config_t* cfg, moe_plan_t* plan, 
 MOE_API moe_status_t moe_plan_destroy(moe_plan_t plan);
 
 /* Enqueue the whole sublayer on `stream` (a hipStream_t; NULL = default stream).
- * num_tokens in [0, max_tokens]; 0 is a successful no-op.  top_k in
- * [1, min(E, max_top_k)].  routed_scale finite.  Shared pointers may be NULL
- * only when the plan's shared_inter is 0.  Returns asynchronously. */
+ * num_tokens in [0, max_tokens]; 0 is a successful no-op that reads no pointer
+ * (they may then be NULL).  top_k in [1, min(E, max_top_k)].  routed_scale
+ * finite.  Shared pointers may be NULL only when the plan's shared_inter is 0.
+ * Returns asynchronously. */
 MOE_API moe_status_t moe_block_forward(moe_plan_t plan, void* workspace, size_t workspace_bytes,
                                void* stream, int64_t num_tokens, const void* x, const void* norm_w,
                                const void* router_w, const float* corr_bias, const void* gate_up,
@@ -161,14 +162,17 @@ MOE_API size_t moe_buffer_bytes(moe_plan_t plan, int64_t num_tokens, int32_t top
 /* Path the plan takes for num_tokens/top_k (MOE_PATH_STREAM or MOE_PATH_MFMA). */
 MOE_API int32_t moe_plan_path(moe_plan_t plan, int64_t num_tokens, int32_t top_k);
 
-/* Per-stage GPU timing.  When enabled on a plan, moe_block_forward records a
- * HIP event before and after each kernel it enqueues; after the caller
- * synchronises, moe_stage_times adds the elapsed milliseconds of every call
- * since the last reset into ms[stage] and the number of calls into *calls.
- * Stage names come from moe_stage_name.  Timing is meant for one thread. */
+/* Per-stage GPU timing.  stage_mask selects stages (bit s = stage s, see
+ * moe_stage_name; 0 disables).  While set, moe_block_forward records a HIP
+ * event before and after each selected stage's kernels on the call's stream;
+ * after the caller synchronises, moe_stage_times returns the elapsed
+ * milliseconds summed per stage since the last read in ms[stage] and the number
+ * of timed calls in *calls.  Timing state is the only mutable part of a plan and
+ * is meant for one thread. */
 #define MOE_MAX_STAGES 16
-MOE_API moe_status_t moe_set_stage_timing(moe_plan_t plan, int32_t enable);
-MOE_API moe_status_t moe_stage_times(moe_plan_t plan, double* ms /*[MOE_MAX_STAGES]*/, int64_t* calls);
+MOE_API moe_status_t moe_set_stage_timing(moe_plan_t plan, int32_t stage_mask);
+MOE_API moe_status_t moe_stage_times(moe_plan_t plan, double* ms /*[MOE_MAX_STAGES]*/,
+                                     int64_t* calls);
 MOE_API const char* moe_stage_name(int32_t stage);
 
 MOE_API const char* moe_status_string(moe_status_t status);

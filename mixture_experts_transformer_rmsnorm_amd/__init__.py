@@ -184,8 +184,19 @@ def moe_plan_path(plan, num_tokens, top_k) -> int:
     return load().moe_plan_path(plan, num_tokens, top_k)
 
 
-def moe_set_stage_timing(plan, enable: bool) -> None:
-    _check(load().moe_set_stage_timing(plan, 1 if enable else 0), "moe_set_stage_timing")
+def moe_set_stage_timing(plan, stage_mask: int) -> None:
+    """Time the stages whose bit is set in stage_mask (0 disables)."""
+    _check(load().moe_set_stage_timing(plan, int(stage_mask)), "moe_set_stage_timing")
+
+
+def stage_mask(*names) -> int:
+    """Bit mask of the named stages (all stages when no name is given)."""
+    mask = 0
+    for i in range(MOE_MAX_STAGES):
+        n = moe_stage_name(i)
+        if n is not None and (not names or n in names):
+            mask |= 1 << i
+    return mask
 
 
 def moe_stage_times(plan):

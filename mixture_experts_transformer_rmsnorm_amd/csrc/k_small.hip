@@ -127,38 +127,58 @@ hipError_t launch_fma_nt(int dtype, const NtArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Router selection.  One wavefront per token: lane l holds experts l, l+64, ...
+// Router selection.  One wavefront per token (a block holds the kChunkTokens
+// tokens of one chunk): lane l holds experts l, l+64, ... (Q per lane).
 // score = sigmoid(logit) in fp32; key = score + corr_bias (fp32) decides the
 // selection; k rounds of a wave-wide arg-max over (key desc, expert asc); the
 // weights are the selected unbiased scores renormalised to sum routed_scale.
 // Each block also writes its chunk's per-expert histogram.
-constexpr int kTopkMaxQ = 16;  // experts per lane: E <= 1024
-
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ part, int splits,
-                                                   const float* __restrict__ bias, int64_t T,
-                                                   int E, int k, float rs,
-                                                   int32_t* __restrict__ idx_out,
-                                                   float* __restrict__ w_out,
-                                                   int32_t* __restrict__ chunk_cnt) {
+template <int Q, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void topk_kernel(const float* __restrict__ part,
+                                                          int splits,
+                                                          const float* __restrict__ bias,
+                                                          int64_t T, int E, int k, float rs,
+                                                          int32_t* __restrict__ idx_out,
+                                                          float* __restrict__ w_out,
+                                                          int32_t* __restrict__ chunk_cnt) {
   __shared__ int hist[1024];
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  const int nq = (E + kWave - 1) / kWave;
   const int64_t tbase = (int64_t)blockIdx.x * kChunkTokens;
-  for (int tl = wid; tl < kChunkTokens; tl += 4) {
+  for (int tl = wid; tl < kChunkTokens; tl += WAVES) {
     const int64_t t = tbase + tl;
     if (t >= T) break;
-    float key[kTopkMaxQ], sc[kTopkMaxQ];
+    float key[Q], sc[Q];
+    float l[Q];
 #pragma unroll
-    for (int q = 0; q < kTopkMaxQ; ++q) {
+    for (int q = 0; q < Q; ++q) l[q] = 0.f;
+    const int64_t zstride = T * (int64_t)E;
+    const float* pt = part + t * E + lane;
+    int z = 0;
+    for (; z + 4 <= splits; z += 4) {
+      float v[4][Q];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+          v[u][q] = (lane + kWave * q < E) ? pt[(z + u) * zstride + kWave * q] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < Q; ++q) l[q] += v[u][q];
+    }
+    for (; z < splits; ++z)
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+        if (lane + kWave * q < E) l[q] += pt[z * zstride + kWave * q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
       const int e = lane + kWave * q;
       key[q] = -INFINITY;
       sc[q] = 0.f;
-      if (q < nq && e < E) {
-        float l = 0.f;
-        for (int z = 0; z < splits; ++z) l += part[((int64_t)z * T + t) * E + e];
-        const float sg = 1.0f / (1.0f + expf(-l));
+      if (e < E) {
+        const float sg = 1.0f / (1.0f + expf(-l[q]));
         sc[q] = sg;
         key[q] = sg + bias[e];
       }
@@ -170,9 +190,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
       float bv = -INFINITY, bs = 0.f;
       int be = 0x7fffffff;
 #pragma unroll
-      for (int q = 0; q < kTopkMaxQ; ++q) {
+      for (int q = 0; q < Q; ++q) {
         const int e = lane + kWave * q;
-        const bool ok = q < nq && e < E && !((taken >> q) & 1u);
+        const bool ok = e < E && !((taken >> q) & 1u);
         if (ok && (key[q] > bv || (key[q] == bv && e < be))) {
           bv = key[q];
           be = e;
@@ -211,9 +231,17 @@ hipError_t launch_topk(const float* logit_part, int splits, const float* corr_bi
                        int E, int k, float routed_scale, int32_t* topk_idx, float* topk_w,
                        int32_t* chunk_cnt, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int64_t nchunks = (T + kChunkTokens - 1) / kChunkTokens;
-  topk_kernel<<<dim3((unsigned)nchunks), 256, 0, s>>>(logit_part, splits, corr_bias, T, E, k,
-                                                      routed_scale, topk_idx, topk_w, chunk_cnt);
+  const dim3 grid((unsigned)((T + kChunkTokens - 1) / kChunkTokens));
+  const int q = (E + kWave - 1) / kWave;
+#define MOE_TOPK(QQ, WW)                                                                    \
+  topk_kernel<QQ, WW><<<grid, WW * 64, 0, s>>>(logit_part, splits, corr_bias, T, E, k,      \
+                                               routed_scale, topk_idx, topk_w, chunk_cnt)
+  if (q <= 1) MOE_TOPK(1, 16);
+  else if (q <= 2) MOE_TOPK(2, 16);
+  else if (q <= 4) MOE_TOPK(4, 16);
+  else if (q <= 8) MOE_TOPK(8, 8);
+  else MOE_TOPK(16, 4);
+#undef MOE_TOPK
   return hipGetLastError();
 }
 

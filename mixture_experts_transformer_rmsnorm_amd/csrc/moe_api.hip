@@ -26,6 +26,9 @@ constexpr int kMaxExperts = 1024;
 constexpr int kStreamMaxMeanTokens = 8;
 // Split-K target: enough blocks for two per compute unit on 256 CUs.
 constexpr int kTargetBlocks = 512;
+// Partial sums the router top-k and the shared-expert consumers add per value.
+constexpr int kMaxRouterSplits = 16;
+constexpr int kMaxSharedSplits = 16;
 
 enum Stage {
   kStNorm = 0,
@@ -54,12 +57,15 @@ struct Split {
   int kt_per;
 };
 
-// Split-K factor for a dense K-contiguous product of M rows, N columns, K depth.
-Split nt_split(int64_t M, int64_t N, int64_t K, int tm, int tn, int tk) {
+// Split-K factor for a dense K-contiguous product of M rows, N columns, K depth:
+// enough blocks to fill the chip, at least two K tiles per split, at most
+// max_splits partial sums for the consumer to add.
+Split nt_split(int64_t M, int64_t N, int64_t K, int tm, int tn, int tk, int max_splits) {
   const int64_t tiles = cdiv(M, tm) * cdiv(N, tn);
   const int64_t nkt = K / tk;
   int64_t s = std::max<int64_t>(1, cdiv(kTargetBlocks, std::max<int64_t>(tiles, 1)));
   s = std::min<int64_t>(s, std::max<int64_t>(1, nkt / 2));
+  s = std::min<int64_t>(s, max_splits);
   const int64_t per = cdiv(nkt, s);
   return Split{(int)cdiv(nkt, per), (int)per};
 }
@@ -82,7 +88,8 @@ struct moe_plan {
   Layout lay;
   // stage timing (the only mutable state of a plan)
   std::mutex tmu;
-  bool timing = false;
+  int32_t timing_mask = 0;
+  int64_t timed_calls = 0;
   std::vector<EventPair> pending;
   std::vector<hipEvent_t> pool;
 };
@@ -108,13 +115,13 @@ void nt_tiles(const moe_plan* p, int* tm, int* tn, int* tk) {
 }
 
 // Largest split-K partial buffer (in fp32 elements) over every T <= Tmax.
-size_t max_partial_elems(const moe_plan* p, int64_t Tmax, int64_t N, int64_t K) {
+size_t max_partial_elems(const moe_plan* p, int64_t Tmax, int64_t N, int64_t K, int max_splits) {
   int tm, tn, tk;
   nt_tiles(p, &tm, &tn, &tk);
   size_t best = 0;
   for (int64_t m = 1; m <= std::max<int64_t>(1, cdiv(Tmax, tm)); ++m) {
     const int64_t T = std::min<int64_t>(m * tm, std::max<int64_t>(Tmax, 1));
-    const Split s = nt_split(T, N, K, tm, tn, tk);
+    const Split s = nt_split(T, N, K, tm, tn, tk, max_splits);
     best = std::max(best, (size_t)s.splits * (size_t)T * (size_t)N);
   }
   return best;
@@ -134,7 +141,7 @@ void make_layout(moe_plan* p) {
   };
   Layout& L = p->lay;
   L.h = take((size_t)T * c.dim * es);
-  L.logits = take(max_partial_elems(p, T, c.n_experts, c.dim) * 4);
+  L.logits = take(max_partial_elems(p, T, c.n_experts, c.dim, kMaxRouterSplits) * 4);
   L.topk_idx = take((size_t)A * 4);
   L.topk_w = take((size_t)A * 4);
   L.chunk_cnt = take((size_t)nch * c.n_experts * 4);
@@ -148,9 +155,9 @@ void make_layout(moe_plan* p) {
   L.act = take((size_t)A * c.moe_inter * es);
   L.y = take((size_t)A * c.dim * es);
   if (c.shared_inter > 0) {
-    L.sh_gu = take(max_partial_elems(p, T, 2 * (int64_t)c.shared_inter, c.dim) * 4);
+    L.sh_gu = take(max_partial_elems(p, T, 2 * (int64_t)c.shared_inter, c.dim, kMaxSharedSplits) * 4);
     L.act_s = take((size_t)T * c.shared_inter * es);
-    L.sh_dn = take(max_partial_elems(p, T, c.dim, c.shared_inter) * 4);
+    L.sh_dn = take(max_partial_elems(p, T, c.dim, c.shared_inter, kMaxSharedSplits) * 4);
   } else {
     L.sh_gu = L.act_s = L.sh_dn = 0;
   }
@@ -236,10 +243,10 @@ int32_t moe_plan_path(moe_plan_t p, int64_t num_tokens, int32_t top_k) {
   return use_mfma(p, num_tokens, top_k) ? MOE_PATH_MFMA : MOE_PATH_STREAM;
 }
 
-moe_status_t moe_set_stage_timing(moe_plan_t p, int32_t enable) {
-  if (!p) return MOE_ERROR_INVALID_VALUE;
+moe_status_t moe_set_stage_timing(moe_plan_t p, int32_t stage_mask) {
+  if (!p || stage_mask < 0 || stage_mask >= (1 << kNumStages)) return MOE_ERROR_INVALID_VALUE;
   std::lock_guard<std::mutex> g(p->tmu);
-  p->timing = enable != 0;
+  p->timing_mask = stage_mask;
   return MOE_SUCCESS;
 }
 
@@ -247,17 +254,18 @@ moe_status_t moe_stage_times(moe_plan_t p, double* ms, int64_t* calls) {
   if (!p || !ms) return MOE_ERROR_INVALID_VALUE;
   std::lock_guard<std::mutex> g(p->tmu);
   for (int i = 0; i < MOE_MAX_STAGES; ++i) ms[i] = 0.0;
-  int64_t n_norm = 0;
   for (auto& ev : p->pending) {
     float t = 0.f;
     if (hipEventElapsedTime(&t, ev.a, ev.b) != hipSuccess) return MOE_ERROR_HIP;
     ms[ev.stage] += t;
-    if (ev.stage == kStNorm) ++n_norm;
+  }
+  for (auto& ev : p->pending) {
     p->pool.push_back(ev.a);
     p->pool.push_back(ev.b);
   }
   p->pending.clear();
-  if (calls) *calls = n_norm;
+  if (calls) *calls = p->timed_calls;
+  p->timed_calls = 0;
   return MOE_SUCCESS;
 }
 
@@ -272,6 +280,7 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   if (T < 0 || T > c.max_tokens) return MOE_ERROR_INVALID_VALUE;
   if (k < 1 || k > c.max_top_k || k > c.n_experts) return MOE_ERROR_INVALID_VALUE;
   if (!isfinite(routed_scale)) return MOE_ERROR_INVALID_VALUE;
+  if (T == 0) return MOE_SUCCESS;  // nothing is read or written
   if (!workspace || !x || !norm_w || !router_w || !corr_bias || !gate_up || !down || !out)
     return MOE_ERROR_INVALID_VALUE;
   const bool has_shared = c.shared_inter > 0;
@@ -281,7 +290,6 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
       (has_shared && (misaligned(shared_gate) || misaligned(shared_up) || misaligned(shared_down))))
     return MOE_ERROR_MISALIGNED;
   if (workspace_bytes < p->lay.total) return MOE_ERROR_WORKSPACE_TOO_SMALL;
-  if (T == 0) return MOE_SUCCESS;
 
   hipStream_t s = (hipStream_t)stream;
   const Layout& L = p->lay;
@@ -313,16 +321,20 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   nt_tiles(p, &tm, &tn, &tk);
 
   std::unique_lock<std::mutex> tlock(p->tmu, std::defer_lock);
-  bool timing = false;
+  int32_t tmask = 0;
   {
     std::lock_guard<std::mutex> g(p->tmu);
-    timing = p->timing;
+    tmask = p->timing_mask;
   }
-  if (timing) tlock.lock();
+  if (tmask) {
+    tlock.lock();
+    ++p->timed_calls;
+  }
   hipError_t err = hipSuccess;
   auto stage = [&](int st, auto&& fn) {
     if (err != hipSuccess) return;
     EventPair ev{st, nullptr, nullptr};
+    const bool timing = (tmask >> st) & 1;
     if (timing) {
       ev.a = get_event(p);
       ev.b = get_event(p);
@@ -341,17 +353,20 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
     }
   };
   auto nt = [&](const void* Aop, int64_t lda, const void* B1, const void* B2, int64_t ldb,
-                int n_split, float* outp, int64_t N, int64_t K) {
-    const Split sp = nt_split(T, N, K, tm, tn, tk);
+                int n_split, float* outp, int64_t N, int64_t K, int max_splits) {
+    const Split sp = nt_split(T, N, K, tm, tn, tk, max_splits);
     NtArgs a{Aop, lda, B1, B2, ldb, n_split, outp, (int)T, (int)N, (int)K, sp.splits, sp.kt_per};
     return dt == kBF16 ? launch_mfma_nt(a, s) : launch_fma_nt(dt, a, s);
   };
-  const Split rsplit = nt_split(T, E, d, tm, tn, tk);
-  const Split sdsplit = has_shared ? nt_split(T, d, Is, tm, tn, tk) : Split{0, 0};
-  const Split sgsplit = has_shared ? nt_split(T, 2 * (int64_t)Is, d, tm, tn, tk) : Split{0, 0};
+  const Split rsplit = nt_split(T, E, d, tm, tn, tk, kMaxRouterSplits);
+  const Split sdsplit =
+      has_shared ? nt_split(T, d, Is, tm, tn, tk, kMaxSharedSplits) : Split{0, 0};
+  const Split sgsplit =
+      has_shared ? nt_split(T, 2 * (int64_t)Is, d, tm, tn, tk, kMaxSharedSplits) : Split{0, 0};
 
   stage(kStNorm, [&] { return launch_rmsnorm(dt, x, norm_w, h, T, d, c.eps, s); });
-  stage(kStRouter, [&] { return nt(h, d, router_w, router_w, d, E, logits, E, d); });
+  stage(kStRouter,
+        [&] { return nt(h, d, router_w, router_w, d, E, logits, E, d, kMaxRouterSplits); });
   stage(kStTopk, [&] {
     return launch_topk(logits, rsplit.splits, corr_bias, T, E, k, routed_scale, topk_idx, topk_w,
                        chunk_cnt, s);
@@ -370,7 +385,10 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   });
   if (has_shared) {
     stage(kStSharedGateUp,
-          [&] { return nt(h, d, shared_gate, shared_up, d, Is, sh_gu, 2 * (int64_t)Is, d); });
+          [&] {
+            return nt(h, d, shared_gate, shared_up, d, Is, sh_gu, 2 * (int64_t)Is, d,
+                      kMaxSharedSplits);
+          });
     stage(kStSharedAct,
           [&] { return launch_swiglu_finalize(dt, sh_gu, sgsplit.splits, T, Is, act_s, s); });
   }
@@ -379,7 +397,9 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
                 : launch_stream_down(dt, g, act, down, y, s);
   });
   if (has_shared)
-    stage(kStSharedDown, [&] { return nt(act_s, Is, shared_down, shared_down, Is, d, sh_dn, d, Is); });
+    stage(kStSharedDown, [&] {
+      return nt(act_s, Is, shared_down, shared_down, Is, d, sh_dn, d, Is, kMaxSharedSplits);
+    });
   stage(kStCombine, [&] {
     return launch_combine(dt, x, sh_dn, has_shared ? sdsplit.splits : 0, y, topk_w, row_of, T, d,
                           k, out, s);

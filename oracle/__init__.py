@@ -58,7 +58,8 @@ def _load():
             lib.oracle_counts.argtypes = [i64, i32, i32, P, P, P]
             lib.oracle_experts.argtypes = [i64, P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P,
                                            P, P, P, P, P, P, P, P, P]
-            for fn in ("oracle_round_to_dtype", "oracle_rmsnorm", "oracle_router_scores",
+            lib.oracle_num_threads.argtypes = []
+            for fn in ("oracle_num_threads", "oracle_round_to_dtype", "oracle_rmsnorm", "oracle_router_scores",
                        "oracle_select", "oracle_counts", "oracle_experts"):
                 getattr(lib, fn).restype = ctypes.c_int
             _lib = lib
@@ -82,6 +83,11 @@ def _storage(a, dtype):
 def _check(rc, what):
     if rc != 0:
         raise ValueError("oracle %s rejected its arguments (rc=%d)" % (what, rc))
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())
 
 
 def round_to_dtype(a, dtype):

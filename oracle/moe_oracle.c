@@ -42,6 +42,7 @@
  * Error behaviour: functions return 0 on success, -1 on a bad argument.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -76,6 +77,9 @@ static float load_elem(const void* p, int64_t i, int dtype) {
   if (dtype == OR_BF16) return bf16_bits_to_float(((const uint16_t*)p)[i]);
   return ((const float*)p)[i];
 }
+
+/* Threads an OpenMP parallel region of this library uses. */
+ORACLE_API int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 ORACLE_API int oracle_round_to_dtype(int64_t n, const float* in, float* out, int dtype) {
   if (n < 0 || (n > 0 && (!in || !out))) return -1;
@@ -147,9 +151,12 @@ ORACLE_API int oracle_select(int64_t T, int32_t E, int32_t k, const float* score
     if (!key || !taken) {
 #pragma omp atomic write
       ok = -1;
-    } else {
+    }
+    /* every thread reaches the worksharing loop; one without buffers skips work */
 #pragma omp for schedule(static)
-      for (int64_t t = 0; t < T; ++t) {
+    for (int64_t t = 0; t < T; ++t) {
+      if (!key || !taken) continue;
+      {
         for (int32_t e = 0; e < E; ++e) {
           key[e] = scores[t * E + e] + corr_bias[e];
           taken[e] = 0;
