@@ -166,6 +166,9 @@ def main():
                     help="second workload of the same shape family reported in the line ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size "
+                         "kernel for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -176,6 +179,15 @@ def main():
     import workloads
 
     torch.cuda.set_device(0)
+    if args.calib_mib:
+        n = args.calib_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: %d bytes read, %d bytes written" % (n, n))
+        del src, dst
     cfg = workloads.config(args.config)
     log("drawing %s inputs on the device" % cfg.name)
     tin = workloads.make_torch(cfg, 0, device="cuda", weights="device")

@@ -15,9 +15,13 @@
 //    to LDS as is.
 //  - N-contiguous ([K, N], the grouped expert layout of
 //    Glm4MoeStateDictAdapter: gate_and_up_projs [E, d, 2I], down_projs
-//    [E, I, d]) is read with 16-byte row loads (4 rows x 8 columns per thread)
-//    and transposed in registers before the LDS store, so the fragment reads
-//    stay 16-byte vector reads.
+//    [E, I, d]) is copied to LDS row by row as loaded (rows padded to 144
+//    elements) and the K-contiguous MFMA fragments are formed by gfx950's
+//    transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group,
+//    output lane i, element j is element i%4 of the 8-byte chunk addressed by
+//    lane 4j + i/4, so lane (g, j, q) addressing row 8g+4h+j, column n+4q makes
+//    lane (g, i) receive B[8g+4h .. 8g+4h+3][n+i].  Two such reads give the
+//    8 K-consecutive values of a fragment.
 // The gate_up tile pairs gate columns [c, c+64) with up columns [I+c, I+c+64)
 // so that silu(gate) * up is formed in registers ("GLM-5 · Input features",
 // excerpt mlp).
@@ -28,10 +32,14 @@ namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int BM = kMfmaBM, BN = kMfmaBN, BK = kMfmaBK;
-constexpr int LDK = BK + 8;  // LDS row stride in elements (144 bytes)
+constexpr int LDK = BK + 8;   // K-contiguous LDS rows: 72 elements (144 bytes)
+constexpr int LDN = BN + 16;  // N-contiguous LDS rows: 144 elements (288 bytes)
 constexpr int kTileElems = BM * LDK;
+static_assert(BK * LDN <= kTileElems, "N-contiguous B tile fits the stage buffer");
 
 enum Epi { kEpiPartialF32 = 0, kEpiSwiGLU = 1, kEpiStore = 2 };
 
@@ -71,14 +79,15 @@ __device__ __forceinline__ int b_local_col(int f, int wn) {
   return (f < 2 ? wn * 32 + f * 16 : 64 + wn * 32 + (f - 2) * 16);
 }
 
-__device__ __forceinline__ uint32_t sel_lo(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t sel_hi(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
-}
-__device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+// B fragment of n-block f from an N-contiguous LDS tile by two transposing reads.
+__device__ __forceinline__ bf16x8_t b_frag_tr(const uint16_t* bs, int ks, int col, int lane) {
+  const int g = lane >> 4, j = (lane & 15) >> 2, q = lane & 3;
+  const uint16_t* p = bs + (ks * 32 + 8 * g + j) * LDN + col + 4 * q;
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * LDN));
+  typedef short s16x8_t __attribute__((ext_vector_type(8)));
+  const s16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
 }
 
 template <bool NN, int EPI>
@@ -143,9 +152,8 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaProblem p) {
       b_src[i] = row + (tid % 8) * 8;
     }
   } else {
-    // 4 consecutive k-rows (kg*4 ..) x 8 columns (ng*8 ..) per thread
-    const int ng = tid % 16, kg = tid / 16;
-    const int lc = ng * 8;
+    // k-rows tid/16 + 16*i, 16-byte column chunk tid%16 of the 128 tile columns
+    const int lc = (tid % 16) * 8;
     int gcol;
     bool ok;
     if (EPI == kEpiSwiGLU) {
@@ -156,11 +164,11 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaProblem p) {
       gcol = n_tile * BN + lc;
       ok = gcol < p.N;
     }
-    const uint16_t* base = p.Bg + (int64_t)e * p.b_stride + (int64_t)(kg * 4) * p.ldb + (ok ? gcol : 0);
+    const uint16_t* base = p.Bg + (int64_t)e * p.b_stride + (int64_t)(tid / 16) * p.ldb + (ok ? gcol : 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       b_ok[i] = ok;
-      b_src[i] = base + (int64_t)i * p.ldb;
+      b_src[i] = base + (int64_t)(16 * i) * p.ldb;
     }
     b_kstride = (int64_t)BK * p.ldb;
   }
@@ -190,21 +198,9 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaProblem p) {
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<uint4*>(bs + (tid / 8 + 32 * i) * LDK + (tid % 8) * 8) = rb[i];
     } else {
-      const int ng = tid % 16, kg = tid / 16;
-      // rb[r] holds row kg*4+r, columns ng*8 .. ng*8+7; write column c as 4 k-values
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int dw = c >> 1;
-        uint32_t lo, hi;
-        if (c & 1) {
-          lo = sel_hi(u4_get(rb[0], dw), u4_get(rb[1], dw));
-          hi = sel_hi(u4_get(rb[2], dw), u4_get(rb[3], dw));
-        } else {
-          lo = sel_lo(u4_get(rb[0], dw), u4_get(rb[1], dw));
-          hi = sel_lo(u4_get(rb[2], dw), u4_get(rb[3], dw));
-        }
-        *reinterpret_cast<uint2*>(bs + (ng * 8 + c) * LDK + kg * 4) = make_uint2(lo, hi);
-      }
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4*>(bs + (tid / 16 + 16 * i) * LDN + (tid % 16) * 8) = rb[i];
     }
   };
 
@@ -231,8 +227,12 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaProblem p) {
         for (int mi = 0; mi < 4; ++mi)
           af[mi] = *reinterpret_cast<const bf16x8_t*>(as + (wm * 64 + mi * 16 + (lane & 15)) * LDK + kof);
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
-          bf[f] = *reinterpret_cast<const bf16x8_t*>(bs + (b_local_col(f, wn) + (lane & 15)) * LDK + kof);
+        for (int f = 0; f < 4; ++f) {
+          if (NN)
+            bf[f] = b_frag_tr(bs, ks, b_local_col(f, wn), lane);
+          else
+            bf[f] = *reinterpret_cast<const bf16x8_t*>(bs + (b_local_col(f, wn) + (lane & 15)) * LDK + kof);
+        }
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
