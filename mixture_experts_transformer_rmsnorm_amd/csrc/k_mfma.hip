@@ -36,6 +36,7 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int BM = kMfmaBM, BN = kMfmaBN, BK = kMfmaBK;
+constexpr int kXcds = 8;  // accelerator complex dies of an MI355X, one L2 each
 constexpr int LDK = BK + 8;   // K-contiguous LDS rows: 72 elements (144 bytes)
 constexpr int LDN = BN + 16;  // N-contiguous LDS rows: 144 elements (288 bytes)
 constexpr int kTileElems = BM * LDK;
@@ -66,6 +67,7 @@ struct MfmaProblem {
   const RouteHeader* hdr;
   const int32_t* offsets;
   const int32_t* counts;
+  int n_tiles;  // N-tiles of a grouped problem
   // dense problems
   int M;
   int kt_per_split;
@@ -98,12 +100,23 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaProblem p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
-  const int n_tile = blockIdx.x;
+  int n_tile = blockIdx.x;
 
   int rows, seg = 0, m0, e = 0;
   if (kGrouped) {
-    const int mt = blockIdx.y;
-    if (mt >= p.hdr->n_mtiles) return;
+    // Work-groups are dispatched round-robin over the 8 XCDs.  Give XCD x the
+    // contiguous range [x*per, (x+1)*per) of the (M-tile, N-tile) pairs that exist,
+    // M-tile major: the N-tiles of one M-tile then share x's L2 for the gathered
+    // A rows, and consecutive M-tiles of one expert share it for B.
+    const int n_tiles = p.n_tiles;
+    const int total = p.hdr->n_mtiles * n_tiles;
+    const int per = (total + kXcds - 1) / kXcds;
+    const int slot = blockIdx.x / kXcds;
+    if (slot >= per) return;
+    const int logical = (blockIdx.x % kXcds) * per + slot;
+    if (logical >= total) return;
+    const int mt = logical / n_tiles;
+    n_tile = logical % n_tiles;
     const int2 tt = p.mtiles[mt];
     e = tt.x;
     m0 = tt.y;
@@ -330,8 +343,9 @@ hipError_t launch_mfma_gate_up(const GroupArgs& g, int max_mtiles, const void* h
   p.counts = g.counts;
   p.C = act;
   p.ldc = g.I;
-  dim3 grid((g.I + 63) / 64, max_mtiles);
-  mfma_kernel<true, kEpiSwiGLU><<<grid, 256, 0, s>>>(p);
+  p.n_tiles = (g.I + 63) / 64;
+  const int64_t blocks = ((int64_t)p.n_tiles * max_mtiles + kXcds - 1) / kXcds * kXcds;
+  mfma_kernel<true, kEpiSwiGLU><<<dim3((unsigned)blocks), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -353,8 +367,9 @@ hipError_t launch_mfma_down(const GroupArgs& g, int max_mtiles, const void* act,
   p.counts = g.counts;
   p.C = y;
   p.ldc = g.d;
-  dim3 grid((g.d + BN - 1) / BN, max_mtiles);
-  mfma_kernel<true, kEpiStore><<<grid, 256, 0, s>>>(p);
+  p.n_tiles = (g.d + BN - 1) / BN;
+  const int64_t blocks = ((int64_t)p.n_tiles * max_mtiles + kXcds - 1) / kXcds * kXcds;
+  mfma_kernel<true, kEpiStore><<<dim3((unsigned)blocks), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
