@@ -78,7 +78,7 @@ __device__ __forceinline__ void stream_pass(const GroupArgs& g, const T* __restr
     for (int k = kb; k < ke; k += V, wp += (int64_t)V * ldw) {
       uint4 wv[V];
 #pragma unroll
-      for (int r = 0; r < V; ++r) wv[r] = ldg16(wp + (int64_t)r * ldw);
+      for (int r = 0; r < V; ++r) wv[r] = ldg16_stream(wp + (int64_t)r * ldw);
       float a[MT][V];
 #pragma unroll
       for (int m = 0; m < MT; ++m) Elem<T>::unpack(ldg16(arow[m] + k), a[m]);
