@@ -65,6 +65,10 @@ def load(path: str = LIB_PATH):
         if not os.path.exists(path):
             raise ImportError("libmoe_mi355x.so not found at %s; build it with "
                               "mixture_experts_transformer_rmsnorm_amd/build.py" % path)
+        # torch ships its own HIP runtime under the same soname; loading torch first
+        # makes the library bind to that one, so both share one runtime (streams,
+        # device pointers).  Loading the library first would bring in a second copy.
+        import torch  # noqa: F401
         lib = ctypes.CDLL(path)
         P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
         lib.moe_plan_create.argtypes = [ctypes.POINTER(moe_config_t), ctypes.POINTER(P),

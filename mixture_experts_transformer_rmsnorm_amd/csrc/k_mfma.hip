@@ -4,7 +4,8 @@
 //
 // Tile: 128 (rows) x 128 (B columns) x 64 (K) per 256-thread block, four
 // wavefronts in a 2 x 2 arrangement, each owning 64 rows x 64 B-columns as
-// 4 x 4 tiles of v_mfma_f32_16x16x32_bf16 (fp32 accumulation).  A and B tiles
+// 2 x 2 tiles of v_mfma_f32_32x32x16_bf16 (fp32 accumulation; on MI355X this
+// form sustains about 2.0 PFLOP/s against about 1.7 for the 16x16x32 form).  A and B tiles
 // are staged in LDS with K contiguous (row stride 72 elements, so the 16-byte
 // fragment reads of 16 consecutive rows hit distinct banks) and double
 // buffered: the global loads of K-tile t+1 are in flight while tile t is
@@ -17,11 +18,12 @@
 //    Glm4MoeStateDictAdapter: gate_and_up_projs [E, d, 2I], down_projs
 //    [E, I, d]) is copied to LDS row by row as loaded (rows padded to 144
 //    elements) and the K-contiguous MFMA fragments are formed by gfx950's
-//    transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group,
+//    transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group G,
 //    output lane i, element j is element i%4 of the 8-byte chunk addressed by
-//    lane 4j + i/4, so lane (g, j, q) addressing row 8g+4h+j, column n+4q makes
-//    lane (g, i) receive B[8g+4h .. 8g+4h+3][n+i].  Two such reads give the
-//    8 K-consecutive values of a fragment.
+//    lane 4j + i/4 of the group.  The 32x32x16 B operand wants lane
+//    l = 32*hk + 16*nb + i to hold B[8hk .. 8hk+7][16nb + i]; so lane (G, j, q)
+//    addresses row 8*(G/2) + 4h + j, column 16*(G%2) + 4q, and two reads
+//    (h = 0, 1) give the 8 K-consecutive values.
 // The gate_up tile pairs gate columns [c, c+64) with up columns [I+c, I+c+64)
 // so that silu(gate) * up is formed in registers ("GLM-5 · Input features",
 // excerpt mlp).
@@ -31,7 +33,7 @@
 namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
@@ -77,14 +79,16 @@ struct MfmaProblem {
 };
 
 __device__ __forceinline__ int b_local_col(int f, int wn) {
-  // B-columns of wave column wn: [wn*32, wn*32+32) and [64+wn*32, 64+wn*32+32)
-  return (f < 2 ? wn * 32 + f * 16 : 64 + wn * 32 + (f - 2) * 16);
+  // B-columns of wave column wn: [wn*32, wn*32+32) (f = 0) and [64+wn*32, 64+wn*32+32)
+  // (f = 1); for SwiGLU tiles these are the matching gate and up columns.
+  return f * 64 + wn * 32;
 }
 
-// B fragment of n-block f from an N-contiguous LDS tile by two transposing reads.
+// 32x16 B fragment (K rows ks*16 .., columns col ..) from an N-contiguous LDS
+// tile by two transposing reads.
 __device__ __forceinline__ bf16x8_t b_frag_tr(const uint16_t* bs, int ks, int col, int lane) {
-  const int g = lane >> 4, j = (lane & 15) >> 2, q = lane & 3;
-  const uint16_t* p = bs + (ks * 32 + 8 * g + j) * LDN + col + 4 * q;
+  const int G = lane >> 4, j = (lane & 15) >> 2, q = lane & 3;
+  const uint16_t* p = bs + (ks * 16 + 8 * (G >> 1) + j) * LDN + col + 16 * (G & 1) + 4 * q;
   const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
   const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * LDN));
   typedef short s16x8_t __attribute__((ext_vector_type(8)));
@@ -132,34 +136,31 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaProblem p) {
 
   // ---- per-thread global load assignments
   // A: rows tid/8 + 32*i, 16-byte chunk tid%8
+  // Rows past the tile's valid rows (and B columns past N) load a valid row
+  // (column) instead: they only feed outputs the epilogue never stores, and
+  // unconditional loads keep the wait counts of the pipeline exact.
   const uint16_t* a_src[4];
-  bool a_ok[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = tid / 8 + 32 * i;
-    a_ok[i] = r < rows;
-    int64_t arow = 0;
-    if (a_ok[i]) {
-      if (kGrouped) {
-        const int64_t prow = seg + m0 + r;
-        arow = p.a_gather ? (int64_t)p.a_gather[prow] : prow;
-      } else {
-        arow = m0 + r;
-      }
+    const int r = min(tid / 8 + 32 * i, rows - 1);
+    int64_t arow;
+    if (kGrouped) {
+      const int64_t prow = seg + m0 + r;
+      arow = p.a_gather ? (int64_t)p.a_gather[prow] : prow;
+    } else {
+      arow = m0 + r;
     }
     a_src[i] = p.A + arow * p.lda + (tid % 8) * 8;
   }
   // B
   const uint16_t* b_src[4];
-  bool b_ok[4];
   int64_t b_kstride = 0;
   if (!NN) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int lc = tid / 8 + 32 * i;
       const int n = n_tile * BN + lc;
-      b_ok[i] = n < p.N;
-      const int nn = b_ok[i] ? n : 0;
+      const int nn = n < p.N ? n : 0;
       const uint16_t* row = nn < p.n_split ? p.B1 + (int64_t)nn * p.ldb
                                            : p.B2 + (int64_t)(nn - p.n_split) * p.ldb;
       b_src[i] = row + (tid % 8) * 8;
@@ -179,10 +180,7 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaProblem p) {
     }
     const uint16_t* base = p.Bg + (int64_t)e * p.b_stride + (int64_t)(tid / 16) * p.ldb + (ok ? gcol : 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      b_ok[i] = ok;
-      b_src[i] = base + (int64_t)(16 * i) * p.ldb;
-    }
+    for (int i = 0; i < 4; ++i) b_src[i] = base + (int64_t)(16 * i) * p.ldb;
     b_kstride = (int64_t)BK * p.ldb;
   }
 
@@ -190,14 +188,13 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaProblem p) {
   auto gload = [&](int kt) {
     const int k0 = kt * BK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = a_ok[i] ? ldg16(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) ra[i] = ldg16(a_src[i] + k0);
     if (!NN) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rb[i] = b_ok[i] ? ldg16(b_src[i] + k0) : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < 4; ++i) rb[i] = ldg16(b_src[i] + k0);
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        rb[i] = b_ok[i] ? ldg16(b_src[i] + (int64_t)kt * b_kstride) : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < 4; ++i) rb[i] = ldg16(b_src[i] + (int64_t)kt * b_kstride);
     }
   };
   auto lstore = [&](int buf) {
@@ -217,11 +214,11 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaProblem p) {
     }
   };
 
-  f32x4_t acc[4][4];
+  f32x16_t acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
   if (kt0 < kt1) {
     gload(kt0);
@@ -233,71 +230,71 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaProblem p) {
       const uint16_t* as = As + buf * kTileElems;
       const uint16_t* bs = Bs + buf * kTileElems;
 #pragma unroll
-      for (int ks = 0; ks < BK / 32; ++ks) {
-        const int kof = ks * 32 + (lane >> 4) * 8;
-        bf16x8_t af[4], bf[4];
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        // 32x16 A fragment: lane holds row lane%32, K elements 8*(lane/32) ..
+        const int kof = ks * 16 + (lane >> 5) * 8;
+        bf16x8_t af[2], bf[2];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-          af[mi] = *reinterpret_cast<const bf16x8_t*>(as + (wm * 64 + mi * 16 + (lane & 15)) * LDK + kof);
+        for (int mi = 0; mi < 2; ++mi)
+          af[mi] = *reinterpret_cast<const bf16x8_t*>(as + (wm * 64 + mi * 32 + (lane & 31)) * LDK + kof);
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
+        for (int f = 0; f < 2; ++f) {
           if (NN)
             bf[f] = b_frag_tr(bs, ks, b_local_col(f, wn), lane);
           else
-            bf[f] = *reinterpret_cast<const bf16x8_t*>(bs + (b_local_col(f, wn) + (lane & 15)) * LDK + kof);
+            bf[f] = *reinterpret_cast<const bf16x8_t*>(bs + (b_local_col(f, wn) + (lane & 31)) * LDK + kof);
         }
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-          for (int f = 0; f < 4; ++f)
-            acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bf[f], acc[mi][f], 0, 0, 0);
+          for (int f = 0; f < 2; ++f)
+            acc[mi][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[f], acc[mi][f], 0, 0, 0);
       }
       if (kt + 1 < kt1) lstore(buf ^ 1);
       __syncthreads();
     }
   }
 
-  // ---- epilogue: lane holds rows (lane/16)*4 + i, column lane%16 of each 16x16 tile
-  const int col16 = lane & 15;
+  // ---- epilogue: in each 32x32 tile, accumulator element i of a lane is row
+  // 8*(i/4) + 4*(lane/32) + i%4, column lane%32
+  const int col32 = lane & 31;
+  auto row_of = [&](int mi, int i) { return wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); };
   if (EPI == kEpiPartialF32) {
     float* out = (float*)p.C + (int64_t)blockIdx.z * p.M * p.N;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const int n = n_tile * BN + b_local_col(f, wn) + col16;
+      for (int f = 0; f < 2; ++f) {
+        const int n = n_tile * BN + b_local_col(f, wn) + col32;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = wm * 64 + mi * 16 + (lane >> 4) * 4 + i;
+        for (int i = 0; i < 16; ++i) {
+          const int r = row_of(mi, i);
           if (r < rows && n < p.N) out[(int64_t)(m0 + r) * p.N + n] = acc[mi][f][i];
         }
       }
   } else if (EPI == kEpiSwiGLU) {
     uint16_t* out = (uint16_t*)p.C;
+    const int c = n_tile * 64 + wn * 32 + col32;  // acc[.][0] gate, acc[.][1] up
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const int c = n_tile * 64 + wn * 32 + f * 16 + col16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = wm * 64 + mi * 16 + (lane >> 4) * 4 + i;
-          if (r < rows && c < p.N) {
-            const float v = silu(acc[mi][f][i]) * acc[mi][f + 2][i];
-            out[(int64_t)(seg + m0 + r) * p.ldc + c] = (uint16_t)f32_to_bf16_bits(v);
-          }
+      for (int i = 0; i < 16; ++i) {
+        const int r = row_of(mi, i);
+        if (r < rows && c < p.N) {
+          const float v = silu(acc[mi][0][i]) * acc[mi][1][i];
+          out[(int64_t)(seg + m0 + r) * p.ldc + c] = (uint16_t)f32_to_bf16_bits(v);
         }
       }
   } else {
     uint16_t* out = (uint16_t*)p.C;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const int c = n_tile * BN + b_local_col(f, wn) + col16;
+      for (int f = 0; f < 2; ++f) {
+        const int c = n_tile * BN + b_local_col(f, wn) + col32;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = wm * 64 + mi * 16 + (lane >> 4) * 4 + i;
+        for (int i = 0; i < 16; ++i) {
+          const int r = row_of(mi, i);
           if (r < rows && c < p.N)
             out[(int64_t)(seg + m0 + r) * p.ldc + c] = (uint16_t)f32_to_bf16_bits(acc[mi][f][i]);
         }
