@@ -30,6 +30,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of `stage` on `workload` from profiles/traffic.txt (rocprofv3
+    FETCH_SIZE + WRITE_SIZE, scaled by a plain-copy calibration), or None when no record
+    exists or the kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        wl, st, files, sha, fetch, write, _alg = line.split()
+        if wl != workload or st != stage:
+            continue
+        h = hashlib.sha256()
+        for f in files.split(","):
+            h.update(open(os.path.join(ROOT, "mixture_experts_transformer_rmsnorm_amd", "csrc", f),
+                          "rb").read())
+        if h.hexdigest()[:16] != sha:
+            return None
+        return int(fetch) + int(write)
+    return None
+
+
 def algorithmic(cfg, counts):
     """Algorithmic HBM bytes and FLOPs of one step and of one gate_up launch."""
     b = 2 if cfg.dtype == "bf16" else 4
@@ -100,8 +124,11 @@ def run_workload(cfg, tin, steps, warmup):
         achieved = alg["gu_flops"] / gu_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    roof["traffic"] = measured_traffic(cfg.name, DOMINANT)
     roof.update(kernel=DOMINANT, kernel_ms=round(gu_ms, 4), algorithmic_bytes=alg["gu_bytes"],
                 algorithmic_flops=alg["gu_flops"], active_experts=alg["n_active"])
+    if roof["traffic"]:
+        roof["traffic_over_algorithmic"] = round(roof["traffic"] / alg["gu_bytes"], 4)
     step_s = ms_step * 1e-3
     hbm_frac = alg["step_bytes"] / step_s / (HBM_PEAK_GBS * 1e9)
     mfma_frac = alg["step_flops"] / step_s / (BF16_PEAK_TFLOPS * 1e12)
