@@ -302,6 +302,234 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaProblem p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Grouped expert kernel (prefill-sized batches).
+//
+// Work unit: one M-tile (up to 256 permuted rows of one expert) x one N-tile
+// (256 B-columns; gate_up: 128 gate columns and the matching 128 up columns).
+// An M-tile holds every row of an expert that has at most 256 rows, so such an
+// expert's weights are read from HBM once.
+//
+// 8 wavefronts per block in a 2 (M) x 4 (N) arrangement.  Wave (wm, wn) owns the
+// 32-row sub-tiles wm, wm+2, wm+4, wm+6 (interleaved, so that a tile with few
+// rows still keeps both row halves of the block busy) and two 32-column groups;
+// sub-tiles past the tile's row count skip their MFMAs.
+//
+// Operands move from global memory straight into LDS (global_load_lds_dwordx4,
+// 16 bytes per lane; the 64 lanes of one instruction fill 1 KiB of LDS in lane
+// order) through a ring of 5 stages of K = 32: while stage t is multiplied,
+// stages t+1..t+4 are in flight.  The ring occupies all 160 KiB of LDS (5 x 32
+// KiB, no padding); bank conflicts are avoided by XOR swizzles applied on the
+// load side (each lane chooses which 16-byte chunk it fetches into its fixed
+// LDS slot):
+//   A stage [256 rows][32 k]: row r, k-chunk c (8 elements) sits at chunk
+//     position c ^ ((r >> 2) & 3) of the 64-byte row;
+//   B stage [32 k][256 n]:   k-row k, n-chunk c sits at position c ^ (4 * (k & 3))
+//     of the 512-byte row.
+// One barrier per stage.  Each stage is its own __shared__ object and the loop
+// is unrolled over the ring, so that the compiler sees that the reads of stage
+// t do not depend on the loads just issued into another stage.
+constexpr int GB_M = kGroupBM, GB_N = 256, GB_K = 32, GB_STAGES = 5, GB_THREADS = 512;
+constexpr int GB_A_ELEMS = GB_M * GB_K, GB_B_ELEMS = GB_K * GB_N;
+constexpr int GB_STAGE_ELEMS = GB_A_ELEMS + GB_B_ELEMS;  // 16384 elements = 32 KiB
+constexpr int GB_ACT_COLS = GB_N / 2;
+constexpr int GB_LOADS_PER_STAGE = 4;  // per thread: 2 A + 2 B instructions
+static_assert(GB_STAGES * GB_STAGE_ELEMS * 2 <= 160 * 1024, "ring fits the LDS of a CU");
+static_assert(GB_A_ELEMS == GB_THREADS * 8 * 2 && GB_B_ELEMS == GB_THREADS * 8 * 2,
+              "each thread moves two 16-byte chunks of A and two of B per stage");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0, expcnt 6:4, lgkmcnt
+// 11:8): wait until at most n vector-memory operations of this wave are
+// outstanding and all of its LDS operations have completed.
+constexpr int waitcnt_vm_lgkm0(int n) { return 0x0070 | n; }
+
+template <int EPI>
+__global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t st0[GB_STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t st1[GB_STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t st2[GB_STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t st3[GB_STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t st4[GB_STAGE_ELEMS];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // (M-tile, N-tile) of this block, XCD-aware as in mfma_kernel
+  const int n_tiles = p.n_tiles;
+  const int total = p.hdr->n_mtiles * n_tiles;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= per) return;
+  const int logical = (blockIdx.x % kXcds) * per + slot;
+  if (logical >= total) return;
+  const int2 tt = p.mtiles[logical / n_tiles];
+  const int n_tile = logical % n_tiles;
+  const int e = tt.x, m0 = tt.y, seg = p.offsets[e];
+  const int rows = min(GB_M, p.counts[e] - m0);
+  const int nkt = p.K / GB_K;
+
+  // ---- load side.  Instruction i (0, 1) of wave w fills 1 KiB of a stage:
+  // A rows 16*(2w+i) + lane/4, chunk position lane%4; B k-rows 2*(2w+i) + lane/32,
+  // chunk position lane%32.  Rows past the tile's end repeat its last row and
+  // columns past N read column 0, so every load is in bounds; what they bring
+  // only reaches outputs that are never stored.
+  const uint16_t* a_src[2];
+  const uint16_t* b_src[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * (2 * w + i) + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const int64_t prow = seg + m0 + min(r, rows - 1);
+    const int64_t arow = p.a_gather ? (int64_t)p.a_gather[prow] : prow;
+    a_src[i] = p.A + arow * p.lda + c * 8;
+
+    const int k = 2 * (2 * w + i) + (lane >> 5);
+    const int cb = (lane & 31) ^ (4 * (k & 3));
+    int gcol;
+    if (EPI == kEpiSwiGLU) {
+      const int col = n_tile * GB_ACT_COLS + (cb & 15) * 8;
+      gcol = col < p.N ? (cb < 16 ? 0 : p.up_off) + col : 0;
+    } else {
+      const int col = n_tile * GB_N + cb * 8;
+      gcol = col < p.N ? col : 0;
+    }
+    b_src[i] = p.Bg + (int64_t)e * p.b_stride + (int64_t)k * p.ldb + gcol;
+  }
+  const int64_t b_kstep = (int64_t)GB_K * p.ldb;
+  auto issue = [&](uint16_t* stage, int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_global_load_lds(a_src[i] + kt * GB_K,
+                                       (lds_void_t*)(stage + (2 * w + i) * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(b_src[i] + kt * b_kstep,
+                                       (lds_void_t*)(stage + GB_A_ELEMS + (2 * w + i) * 512), 16,
+                                       0, 0);
+    }
+  };
+
+  // ---- compute side
+  const int wm = w >> 2, wn = w & 3;
+  auto bcol = [&](int f) { return EPI == kEpiSwiGLU ? f * GB_ACT_COLS + wn * 32 : wn * 64 + f * 32; };
+  bool sub_ok[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sub_ok[j] = 32 * (wm + 2 * j) < rows;
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int f = 0; f < 2; ++f) acc[j][f] = f32x16_t{};
+
+  // per-lane LDS element offsets inside a stage (the same for every stage)
+  int a_off[4][2];  // [sub-tile][k-substep of 16]
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int r = 32 * (wm + 2 * j) + (lane & 31);
+      const int c = 2 * ks + (lane >> 5);
+      a_off[j][ks] = r * GB_K + ((c ^ ((r >> 2) & 3)) * 8);
+    }
+  // B fragment of column group f, k-substep ks: two transposing reads, the second
+  // 4 k-rows further on (same swizzle, since (k + 4) & 3 == k & 3).
+  int b_off[2][2];
+  {
+    const int G = lane >> 4, j4 = (lane & 15) >> 2, q = lane & 3;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int k = ks * 16 + 8 * (G >> 1) + j4;
+        const int c = bcol(f) / 8 + 2 * (G & 1) + (q >> 1);
+        b_off[f][ks] = GB_A_ELEMS + k * GB_N + ((c ^ (4 * (k & 3))) * 8) + (q & 1) * 4;
+      }
+  }
+
+  auto compute = [&](const uint16_t* stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t bf[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const uint16_t* bp = stage + b_off[f][ks];
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)bp);
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(bp + 4 * GB_N));
+        typedef short s16x8_t __attribute__((ext_vector_type(8)));
+        const s16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        bf[f] = __builtin_bit_cast(bf16x8_t, v);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (!sub_ok[j]) continue;
+        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(stage + a_off[j][ks]);
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+          acc[j][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[f], acc[j][f], 0, 0, 0);
+      }
+    }
+  };
+
+  // Step t: wait for this wave's loads of stage t (the 3 later stages may stay
+  // in flight), barrier (every wave's stage-t data has landed and every wave is
+  // done with the slot of stage t-1), refill that slot with stage t+4, multiply
+  // stage t.  Stages past the end are requested too (as copies of the last one)
+  // so that every step has the same number of loads in flight; they land in
+  // slots that are never read again.
+  auto step = [&](const uint16_t* cur, uint16_t* refill, int t) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((GB_STAGES - 2) * GB_LOADS_PER_STAGE));
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    issue(refill, min(t + GB_STAGES - 1, nkt - 1));
+    compute(cur);
+  };
+
+  issue(st0, 0);
+  issue(st1, min(1, nkt - 1));
+  issue(st2, min(2, nkt - 1));
+  issue(st3, min(3, nkt - 1));
+  int t = 0;
+  for (; t + GB_STAGES <= nkt; t += GB_STAGES) {
+    step(st0, st4, t);
+    step(st1, st0, t + 1);
+    step(st2, st1, t + 2);
+    step(st3, st2, t + 3);
+    step(st4, st3, t + 4);
+  }
+  if (t < nkt) step(st0, st4, t);
+  if (t + 1 < nkt) step(st1, st0, t + 1);
+  if (t + 2 < nkt) step(st2, st1, t + 2);
+  if (t + 3 < nkt) step(st3, st2, t + 3);
+  // no load may still be writing LDS when the block ends
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+
+  const int col32 = lane & 31;
+  uint16_t* out = (uint16_t*)p.C;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (!sub_ok[j]) continue;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * (wm + 2 * j) + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if (r >= rows) continue;
+      uint16_t* orow = out + (int64_t)(seg + m0 + r) * p.ldc;
+      if (EPI == kEpiSwiGLU) {
+        const int c = n_tile * GB_ACT_COLS + wn * 32 + col32;
+        if (c < p.N) orow[c] = (uint16_t)f32_to_bf16_bits(silu(acc[j][0][i]) * acc[j][1][i]);
+      } else {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const int c = n_tile * GB_N + bcol(f) + col32;
+          if (c < p.N) orow[c] = (uint16_t)f32_to_bf16_bits(acc[j][f][i]);
+        }
+      }
+    }
+  }
+}
+
 hipError_t launch_mfma_nt(const NtArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   MfmaProblem p = {};
@@ -340,9 +568,9 @@ hipError_t launch_mfma_gate_up(const GroupArgs& g, int max_mtiles, const void* h
   p.counts = g.counts;
   p.C = act;
   p.ldc = g.I;
-  p.n_tiles = (g.I + 63) / 64;
+  p.n_tiles = (g.I + GB_ACT_COLS - 1) / GB_ACT_COLS;
   const int64_t blocks = ((int64_t)p.n_tiles * max_mtiles + kXcds - 1) / kXcds * kXcds;
-  mfma_kernel<true, kEpiSwiGLU><<<dim3((unsigned)blocks), 256, 0, s>>>(p);
+  mfma_grouped_kernel<kEpiSwiGLU><<<dim3((unsigned)blocks), GB_THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -364,9 +592,9 @@ hipError_t launch_mfma_down(const GroupArgs& g, int max_mtiles, const void* act,
   p.counts = g.counts;
   p.C = y;
   p.ldc = g.d;
-  p.n_tiles = (g.d + BN - 1) / BN;
+  p.n_tiles = (g.d + GB_N - 1) / GB_N;
   const int64_t blocks = ((int64_t)p.n_tiles * max_mtiles + kXcds - 1) / kXcds * kXcds;
-  mfma_kernel<true, kEpiStore><<<dim3((unsigned)blocks), 256, 0, s>>>(p);
+  mfma_grouped_kernel<kEpiStore><<<dim3((unsigned)blocks), GB_THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 

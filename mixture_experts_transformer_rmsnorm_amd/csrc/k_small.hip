@@ -281,7 +281,7 @@ __global__ __launch_bounds__(1024) void scan_experts_kernel(const int32_t* __res
   const int e = threadIdx.x;
   const int c = e < E ? counts[e] : 0;
   const int a = c > 0 ? 1 : 0;
-  const int tl = (c + kMfmaBM - 1) / kMfmaBM;
+  const int tl = (c + kGroupBM - 1) / kGroupBM;
   s_cnt[e] = c;
   s_act[e] = a;
   s_til[e] = tl;
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(1024) void scan_experts_kernel(const int32_t* __res
     offsets[e] = s_cnt[e] - c;
     if (a) active[s_act[e] - 1] = e;
     const int t0 = s_til[e] - tl;
-    for (int i = 0; i < tl; ++i) mtiles[t0 + i] = make_int2(e, i * kMfmaBM);
+    for (int i = 0; i < tl; ++i) mtiles[t0 + i] = make_int2(e, i * kGroupBM);
   }
   if (e == E - 1) {
     offsets[E] = s_cnt[e];

@@ -11,8 +11,11 @@ enum DType { kF32 = 0, kBF16 = 1 };
 
 // Tokens handled by one block of the top-k and scatter kernels (one "chunk").
 constexpr int kChunkTokens = 16;
-// Rows per M-tile of the grouped MFMA kernels.
+// Rows per M-tile of the dense MFMA kernel.
 constexpr int kMfmaBM = 128;
+// Rows per M-tile of the grouped expert MFMA kernel: an expert's rows are cut
+// into tiles of this many rows.
+constexpr int kGroupBM = 256;
 // B-columns per N-tile of the MFMA kernels (gate+up halves for SwiGLU).
 constexpr int kMfmaBN = 128;
 constexpr int kMfmaBK = 64;
@@ -22,7 +25,7 @@ constexpr int kFmaTile = 32;
 // Device-side routing summary written by the scan kernel.
 struct RouteHeader {
   int32_t n_active;  // experts with at least one token
-  int32_t n_mtiles;  // M-tiles of kMfmaBM rows over all experts
+  int32_t n_mtiles;  // M-tiles of kGroupBM rows over all experts
   int32_t pad[14];
 };
 

@@ -149,7 +149,7 @@ void make_layout(moe_plan* p) {
   L.offsets = take((size_t)(c.n_experts + 1) * 4);
   L.hdr = take(sizeof(RouteHeader));
   L.active = take((size_t)c.n_experts * 4);
-  L.mtiles = take((size_t)(cdiv(A, kMfmaBM) + std::min<int64_t>(c.n_experts, A)) * sizeof(int2));
+  L.mtiles = take((size_t)(cdiv(A, kGroupBM) + std::min<int64_t>(c.n_experts, A)) * sizeof(int2));
   L.perm_token = take((size_t)A * 4);
   L.row_of = take((size_t)A * 4);
   L.act = take((size_t)A * c.moe_inter * es);
@@ -378,7 +378,7 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
     return launch_scatter(topk_idx, chunk_cnt, offsets, T, E, k, perm_token, row_of, s);
   });
   GroupArgs g{counts, offsets, hdr, active, mtiles, perm_token, E, d, I};
-  const int max_mtiles = (int)(cdiv(A, kMfmaBM) + std::min<int64_t>(E, A));
+  const int max_mtiles = (int)(cdiv(A, kGroupBM) + std::min<int64_t>(E, A));
   stage(kStGateUp, [&] {
     return mfma ? launch_mfma_gate_up(g, max_mtiles, h, gate_up, act, s)
                 : launch_stream_gate_up(dt, g, h, gate_up, act, s);
