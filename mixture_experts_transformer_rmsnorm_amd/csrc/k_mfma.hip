@@ -1,32 +1,34 @@
-// bf16 matrix-core (MFMA) kernels for gfx950: the grouped expert matmuls of
-// prefill-sized batches and the dense K-contiguous products (router logits,
-// shared expert).
+// bf16 matrix-core (MFMA) kernels for gfx950: the dense K-contiguous products
+// (router logits, shared expert) and the grouped expert matmuls of
+// prefill-sized batches.  Both use v_mfma_f32_32x32x16_bf16 (fp32
+// accumulation; on MI355X this form sustains about 2.0 PFLOP/s against about
+// 1.7 for the 16x16x32 form).  In a 32x32 accumulator tile, element i of lane l
+// is row 8*(i/4) + 4*(l/32) + i%4, column l%32; the A operand lane l holds row
+// l%32, K elements 8*(l/32) .. +7, and the B operand lane l holds column l%32,
+// the same K elements.
 //
-// Tile: 128 (rows) x 128 (B columns) x 64 (K) per 256-thread block, four
-// wavefronts in a 2 x 2 arrangement, each owning 64 rows x 64 B-columns as
-// 2 x 2 tiles of v_mfma_f32_32x32x16_bf16 (fp32 accumulation; on MI355X this
-// form sustains about 2.0 PFLOP/s against about 1.7 for the 16x16x32 form).  A and B tiles
-// are staged in LDS with K contiguous (row stride 72 elements, so the 16-byte
-// fragment reads of 16 consecutive rows hit distinct banks) and double
-// buffered: the global loads of K-tile t+1 are in flight while tile t is
-// multiplied.
+// Dense kernel (mfma_nt_kernel): out_part[z] = A[M, K] . B[N, K]^T over the K
+// range of split z, fp32 partials.  Tile 128 x 128 x 64 per 256-thread block,
+// four wavefronts in a 2 x 2 arrangement, each owning 64 rows x 64 columns as
+// 2 x 2 MFMA tiles.  A and B tiles are staged in LDS with K contiguous (row
+// stride 72 elements, so the 16-byte fragment reads of 16 consecutive rows hit
+// distinct banks) and double buffered: the global loads of K-tile t+1 are in
+// flight while tile t is multiplied.
 //
-// B layouts:
-//  - K-contiguous ([N, K], nn.Linear weights: router, shared expert) is copied
-//    to LDS as is.
-//  - N-contiguous ([K, N], the grouped expert layout of
-//    Glm4MoeStateDictAdapter: gate_and_up_projs [E, d, 2I], down_projs
-//    [E, I, d]) is copied to LDS row by row as loaded (rows padded to 144
-//    elements) and the K-contiguous MFMA fragments are formed by gfx950's
-//    transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group G,
-//    output lane i, element j is element i%4 of the 8-byte chunk addressed by
-//    lane 4j + i/4 of the group.  The 32x32x16 B operand wants lane
-//    l = 32*hk + 16*nb + i to hold B[8hk .. 8hk+7][16nb + i]; so lane (G, j, q)
-//    addresses row 8*(G/2) + 4h + j, column 16*(G%2) + 4q, and two reads
-//    (h = 0, 1) give the 8 K-consecutive values.
-// The gate_up tile pairs gate columns [c, c+64) with up columns [I+c, I+c+64)
+// Grouped kernel (mfma_grouped_kernel): see its own description below.  Its
+// weights are N-contiguous ([K, N], the grouped expert layout of
+// Glm4MoeStateDictAdapter: gate_and_up_projs [E, d, 2I], down_projs [E, I, d]);
+// the K-contiguous B fragments are formed by gfx950's transposing LDS read
+// (ds_read_b64_tr_b16): within each 16-lane group G, output lane i, element j
+// is element i%4 of the 8-byte chunk addressed by lane 4j + i/4 of the group.
+// The 32x32x16 B operand wants lane l = 32*hk + 16*nb + i to hold
+// B[8hk .. 8hk+7][16nb + i]; so lane (G, j, q) addresses k-row 8*(G/2) + 4h + j,
+// column 16*(G%2) + 4q, and two reads (h = 0, 1) give the 8 K-consecutive values.
+// A gate_up tile pairs gate columns [c, c+128) with up columns [I+c, I+c+128)
 // so that silu(gate) * up is formed in registers ("GLM-5 · Input features",
 // excerpt mlp).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -37,14 +39,9 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-constexpr int BM = kMfmaBM, BN = kMfmaBN, BK = kMfmaBK;
 constexpr int kXcds = 8;  // accelerator complex dies of an MI355X, one L2 each
-constexpr int LDK = BK + 8;   // K-contiguous LDS rows: 72 elements (144 bytes)
-constexpr int LDN = BN + 16;  // N-contiguous LDS rows: 144 elements (288 bytes)
-constexpr int kTileElems = BM * LDK;
-static_assert(BK * LDN <= kTileElems, "N-contiguous B tile fits the stage buffer");
 
-enum Epi { kEpiPartialF32 = 0, kEpiSwiGLU = 1, kEpiStore = 2 };
+enum Epi { kEpiSwiGLU = 1, kEpiStore = 2 };
 
 struct MfmaProblem {
   // A rows (K-contiguous): dense rows m, or grouped permuted rows gathered
@@ -52,12 +49,12 @@ struct MfmaProblem {
   const uint16_t* A;
   int64_t lda;
   const int32_t* a_gather;
-  // B, K-contiguous: row n at B1 + n*ldb (n < n_split) else B2 + (n-n_split)*ldb.
+  // dense B, K-contiguous: row n at B1 + n*ldb (n < n_split) else B2 + (n-n_split)*ldb.
   const uint16_t* B1;
   const uint16_t* B2;
   int64_t ldb;
   int n_split;
-  // B, N-contiguous grouped: element (k, n) of expert e at Bg + e*b_stride + k*ldb + n;
+  // grouped B, N-contiguous: element (k, n) of expert e at Bg + e*b_stride + k*ldb + n;
   // SwiGLU up columns start at column up_off.
   const uint16_t* Bg;
   int64_t b_stride;
@@ -78,139 +75,61 @@ struct MfmaProblem {
   int64_t ldc;
 };
 
-__device__ __forceinline__ int b_local_col(int f, int wn) {
-  // B-columns of wave column wn: [wn*32, wn*32+32) (f = 0) and [64+wn*32, 64+wn*32+32)
-  // (f = 1); for SwiGLU tiles these are the matching gate and up columns.
-  return f * 64 + wn * 32;
-}
+// ---------------------------------------------------------------------------
+// Dense kernel
+constexpr int BM = kMfmaBM, BN = kMfmaBN, BK = kMfmaBK;
+constexpr int LDK = BK + 8;  // K-contiguous LDS rows: 72 elements (144 bytes)
+constexpr int kTileElems = BM * LDK;
 
-// 32x16 B fragment (K rows ks*16 .., columns col ..) from an N-contiguous LDS
-// tile by two transposing reads.
-__device__ __forceinline__ bf16x8_t b_frag_tr(const uint16_t* bs, int ks, int col, int lane) {
-  const int G = lane >> 4, j = (lane & 15) >> 2, q = lane & 3;
-  const uint16_t* p = bs + (ks * 16 + 8 * (G >> 1) + j) * LDN + col + 16 * (G & 1) + 4 * q;
-  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
-  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * LDN));
-  typedef short s16x8_t __attribute__((ext_vector_type(8)));
-  const s16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8_t, v);
-}
+// B-columns of wave column wn: [wn*32, wn*32+32) (f = 0) and [64+wn*32, 64+wn*32+32) (f = 1)
+__device__ __forceinline__ int b_local_col(int f, int wn) { return f * 64 + wn * 32; }
 
-template <bool NN, int EPI>
-__global__ __launch_bounds__(256) void mfma_kernel(MfmaProblem p) {
+__global__ __launch_bounds__(256) void mfma_nt_kernel(MfmaProblem p) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2 * kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2 * kTileElems];
-  constexpr bool kGrouped = NN;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
-  int n_tile = blockIdx.x;
-
-  int rows, seg = 0, m0, e = 0;
-  if (kGrouped) {
-    // Work-groups are dispatched round-robin over the 8 XCDs.  Give XCD x the
-    // contiguous range [x*per, (x+1)*per) of the (M-tile, N-tile) pairs that exist,
-    // M-tile major: the N-tiles of one M-tile then share x's L2 for the gathered
-    // A rows, and consecutive M-tiles of one expert share it for B.
-    const int n_tiles = p.n_tiles;
-    const int total = p.hdr->n_mtiles * n_tiles;
-    const int per = (total + kXcds - 1) / kXcds;
-    const int slot = blockIdx.x / kXcds;
-    if (slot >= per) return;
-    const int logical = (blockIdx.x % kXcds) * per + slot;
-    if (logical >= total) return;
-    const int mt = logical / n_tiles;
-    n_tile = logical % n_tiles;
-    const int2 tt = p.mtiles[mt];
-    e = tt.x;
-    m0 = tt.y;
-    seg = p.offsets[e];
-    rows = min(BM, p.counts[e] - m0);
-  } else {
-    m0 = blockIdx.y * BM;
-    rows = min(BM, p.M - m0);
-  }
+  const int n_tile = blockIdx.x;
+  const int m0 = blockIdx.y * BM;
+  const int rows = min(BM, p.M - m0);
   const int nkt = p.K / BK;
-  const int kt0 = kGrouped ? 0 : blockIdx.z * p.kt_per_split;
-  const int kt1 = kGrouped ? nkt : min(nkt, kt0 + p.kt_per_split);
+  const int kt0 = blockIdx.z * p.kt_per_split;
+  const int kt1 = min(nkt, kt0 + p.kt_per_split);
 
-  // ---- per-thread global load assignments
-  // A: rows tid/8 + 32*i, 16-byte chunk tid%8
-  // Rows past the tile's valid rows (and B columns past N) load a valid row
-  // (column) instead: they only feed outputs the epilogue never stores, and
-  // unconditional loads keep the wait counts of the pipeline exact.
+  // ---- per-thread global load assignments: A rows and B rows tid/8 + 32*i,
+  // 16-byte chunk tid%8.  Rows past the tile's valid rows (and B rows past N)
+  // load a valid row instead: they only feed outputs the epilogue never
+  // stores, and unconditional loads keep the wait counts of the pipeline exact.
   const uint16_t* a_src[4];
+  const uint16_t* b_src[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = min(tid / 8 + 32 * i, rows - 1);
-    int64_t arow;
-    if (kGrouped) {
-      const int64_t prow = seg + m0 + r;
-      arow = p.a_gather ? (int64_t)p.a_gather[prow] : prow;
-    } else {
-      arow = m0 + r;
-    }
-    a_src[i] = p.A + arow * p.lda + (tid % 8) * 8;
-  }
-  // B
-  const uint16_t* b_src[4];
-  int64_t b_kstride = 0;
-  if (!NN) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int lc = tid / 8 + 32 * i;
-      const int n = n_tile * BN + lc;
-      const int nn = n < p.N ? n : 0;
-      const uint16_t* row = nn < p.n_split ? p.B1 + (int64_t)nn * p.ldb
-                                           : p.B2 + (int64_t)(nn - p.n_split) * p.ldb;
-      b_src[i] = row + (tid % 8) * 8;
-    }
-  } else {
-    // k-rows tid/16 + 16*i, 16-byte column chunk tid%16 of the 128 tile columns
-    const int lc = (tid % 16) * 8;
-    int gcol;
-    bool ok;
-    if (EPI == kEpiSwiGLU) {
-      const int c = n_tile * 64 + (lc & 63);
-      ok = c < p.N;
-      gcol = (lc < 64 ? 0 : p.up_off) + c;
-    } else {
-      gcol = n_tile * BN + lc;
-      ok = gcol < p.N;
-    }
-    const uint16_t* base = p.Bg + (int64_t)e * p.b_stride + (int64_t)(tid / 16) * p.ldb + (ok ? gcol : 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) b_src[i] = base + (int64_t)(16 * i) * p.ldb;
-    b_kstride = (int64_t)BK * p.ldb;
+    a_src[i] = p.A + (int64_t)(m0 + r) * p.lda + (tid % 8) * 8;
+    const int n = n_tile * BN + tid / 8 + 32 * i;
+    const int nn = n < p.N ? n : 0;
+    const uint16_t* row = nn < p.n_split ? p.B1 + (int64_t)nn * p.ldb
+                                         : p.B2 + (int64_t)(nn - p.n_split) * p.ldb;
+    b_src[i] = row + (tid % 8) * 8;
   }
 
   uint4 ra[4], rb[4];
   auto gload = [&](int kt) {
     const int k0 = kt * BK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = ldg16(a_src[i] + k0);
-    if (!NN) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rb[i] = ldg16(b_src[i] + k0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rb[i] = ldg16(b_src[i] + (int64_t)kt * b_kstride);
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = ldg16(a_src[i] + k0);
+      rb[i] = ldg16(b_src[i] + k0);
     }
   };
   auto lstore = [&](int buf) {
     uint16_t* as = As + buf * kTileElems;
     uint16_t* bs = Bs + buf * kTileElems;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
       *reinterpret_cast<uint4*>(as + (tid / 8 + 32 * i) * LDK + (tid % 8) * 8) = ra[i];
-    if (!NN) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint4*>(bs + (tid / 8 + 32 * i) * LDK + (tid % 8) * 8) = rb[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint4*>(bs + (tid / 16 + 16 * i) * LDN + (tid % 16) * 8) = rb[i];
+      *reinterpret_cast<uint4*>(bs + (tid / 8 + 32 * i) * LDK + (tid % 8) * 8) = rb[i];
     }
   };
 
@@ -231,19 +150,14 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaProblem p) {
       const uint16_t* bs = Bs + buf * kTileElems;
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
-        // 32x16 A fragment: lane holds row lane%32, K elements 8*(lane/32) ..
         const int kof = ks * 16 + (lane >> 5) * 8;
         bf16x8_t af[2], bf[2];
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
           af[mi] = *reinterpret_cast<const bf16x8_t*>(as + (wm * 64 + mi * 32 + (lane & 31)) * LDK + kof);
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          if (NN)
-            bf[f] = b_frag_tr(bs, ks, b_local_col(f, wn), lane);
-          else
-            bf[f] = *reinterpret_cast<const bf16x8_t*>(bs + (b_local_col(f, wn) + (lane & 31)) * LDK + kof);
-        }
+        for (int f = 0; f < 2; ++f)
+          bf[f] = *reinterpret_cast<const bf16x8_t*>(bs + (b_local_col(f, wn) + (lane & 31)) * LDK + kof);
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -255,51 +169,19 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaProblem p) {
     }
   }
 
-  // ---- epilogue: in each 32x32 tile, accumulator element i of a lane is row
-  // 8*(i/4) + 4*(lane/32) + i%4, column lane%32
   const int col32 = lane & 31;
-  auto row_of = [&](int mi, int i) { return wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); };
-  if (EPI == kEpiPartialF32) {
-    float* out = (float*)p.C + (int64_t)blockIdx.z * p.M * p.N;
+  float* out = (float*)p.C + (int64_t)blockIdx.z * p.M * p.N;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const int n = n_tile * BN + b_local_col(f, wn) + col32;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = row_of(mi, i);
-          if (r < rows && n < p.N) out[(int64_t)(m0 + r) * p.N + n] = acc[mi][f][i];
-        }
-      }
-  } else if (EPI == kEpiSwiGLU) {
-    uint16_t* out = (uint16_t*)p.C;
-    const int c = n_tile * 64 + wn * 32 + col32;  // acc[.][0] gate, acc[.][1] up
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int f = 0; f < 2; ++f) {
+      const int n = n_tile * BN + b_local_col(f, wn) + col32;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int r = row_of(mi, i);
-        if (r < rows && c < p.N) {
-          const float v = silu(acc[mi][0][i]) * acc[mi][1][i];
-          out[(int64_t)(seg + m0 + r) * p.ldc + c] = (uint16_t)f32_to_bf16_bits(v);
-        }
+        const int r = wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        if (r < rows && n < p.N) out[(int64_t)(m0 + r) * p.N + n] = acc[mi][f][i];
       }
-  } else {
-    uint16_t* out = (uint16_t*)p.C;
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const int c = n_tile * BN + b_local_col(f, wn) + col32;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = row_of(mi, i);
-          if (r < rows && c < p.N)
-            out[(int64_t)(seg + m0 + r) * p.ldc + c] = (uint16_t)f32_to_bf16_bits(acc[mi][f][i]);
-        }
-      }
-  }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -317,26 +199,28 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaProblem p) {
 //
 // Operands move from global memory straight into LDS (global_load_lds_dwordx4,
 // 16 bytes per lane; the 64 lanes of one instruction fill 1 KiB of LDS in lane
-// order) through a ring of 5 stages of K = 32: while stage t is multiplied,
-// stages t+1..t+4 are in flight.  The ring occupies all 160 KiB of LDS (5 x 32
-// KiB, no padding); bank conflicts are avoided by XOR swizzles applied on the
-// load side (each lane chooses which 16-byte chunk it fetches into its fixed
-// LDS slot):
-//   A stage [256 rows][32 k]: row r, k-chunk c (8 elements) sits at chunk
-//     position c ^ ((r >> 2) & 3) of the 64-byte row;
-//   B stage [32 k][256 n]:   k-row k, n-chunk c sits at position c ^ (4 * (k & 3))
+// order), in K-steps of 64, through two rings that together fill the 160 KiB
+// of LDS: A (activations, mostly L2 hits) has 2 slots of 256 x 64, B (weights,
+// streamed from HBM) has 3 slots of 64 x 256.  While step t is multiplied, A of
+// step t+1 and B of steps t+1 and t+2 are in flight.  A rows are fetched as
+// whole 128-byte lines, and the A loads of 8-row groups that lie entirely past
+// the tile's rows are skipped.  Bank conflicts are avoided by XOR swizzles
+// applied on the load side (each lane chooses which 16-byte chunk it fetches
+// into its fixed LDS slot):
+//   A slot [256 rows][64 k]: row r, k-chunk c (8 elements) sits at chunk
+//     position c ^ ((r >> 1) & 7) of the 128-byte row;
+//   B slot [64 k][256 n]:    k-row k, n-chunk c sits at position c ^ (4 * (k & 3))
 //     of the 512-byte row.
-// One barrier per stage.  Each stage is its own __shared__ object and the loop
-// is unrolled over the ring, so that the compiler sees that the reads of stage
-// t do not depend on the loads just issued into another stage.
-constexpr int GB_M = kGroupBM, GB_N = 256, GB_K = 32, GB_STAGES = 5, GB_THREADS = 512;
-constexpr int GB_A_ELEMS = GB_M * GB_K, GB_B_ELEMS = GB_K * GB_N;
-constexpr int GB_STAGE_ELEMS = GB_A_ELEMS + GB_B_ELEMS;  // 16384 elements = 32 KiB
+// One barrier per K-step.  Each slot is its own __shared__ object and the loop
+// is unrolled over both rings (6 steps), so that the compiler sees that the
+// reads of step t do not depend on the loads just issued into other slots.
+constexpr int GB_M = kGroupBM, GB_N = 256, GB_K = 64, GB_THREADS = 512;
+constexpr int GB_A_ELEMS = GB_M * GB_K, GB_B_ELEMS = GB_K * GB_N;  // 32 KiB each
 constexpr int GB_ACT_COLS = GB_N / 2;
-constexpr int GB_LOADS_PER_STAGE = 4;  // per thread: 2 A + 2 B instructions
-static_assert(GB_STAGES * GB_STAGE_ELEMS * 2 <= 160 * 1024, "ring fits the LDS of a CU");
-static_assert(GB_A_ELEMS == GB_THREADS * 8 * 2 && GB_B_ELEMS == GB_THREADS * 8 * 2,
-              "each thread moves two 16-byte chunks of A and two of B per stage");
+constexpr int GB_A_LOADS = GB_A_ELEMS / (GB_THREADS * 8);  // per thread and step: 4
+constexpr int GB_B_LOADS = GB_B_ELEMS / (GB_THREADS * 8);  // 4
+static_assert((2 * GB_A_ELEMS + 3 * GB_B_ELEMS) * 2 <= 160 * 1024, "rings fit the LDS of a CU");
+static_assert(GB_A_LOADS == 4 && GB_B_LOADS == 4, "load assignment below");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -347,16 +231,19 @@ constexpr int waitcnt_vm_lgkm0(int n) { return 0x0070 | n; }
 
 template <int EPI>
 __global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p) {
-  __shared__ __attribute__((aligned(1024))) uint16_t st0[GB_STAGE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t st1[GB_STAGE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t st2[GB_STAGE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t st3[GB_STAGE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t st4[GB_STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sa0[GB_A_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sa1[GB_A_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sb0[GB_B_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sb1[GB_B_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sb2[GB_B_ELEMS];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // (M-tile, N-tile) of this block, XCD-aware as in mfma_kernel
+  // (M-tile, N-tile) of this block.  Work-groups are dispatched round-robin over
+  // the 8 XCDs; XCD x gets the contiguous range [x*per, (x+1)*per) of the
+  // (M-tile, N-tile) pairs that exist, M-tile major, so that the N-tiles of one
+  // M-tile share x's L2 for the gathered A rows.
   const int n_tiles = p.n_tiles;
   const int total = p.hdr->n_mtiles * n_tiles;
   const int per = (total + kXcds - 1) / kXcds;
@@ -370,22 +257,29 @@ __global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p)
   const int rows = min(GB_M, p.counts[e] - m0);
   const int nkt = p.K / GB_K;
 
-  // ---- load side.  Instruction i (0, 1) of wave w fills 1 KiB of a stage:
-  // A rows 16*(2w+i) + lane/4, chunk position lane%4; B k-rows 2*(2w+i) + lane/32,
-  // chunk position lane%32.  Rows past the tile's end repeat its last row and
-  // columns past N read column 0, so every load is in bounds; what they bring
-  // only reaches outputs that are never stored.
-  const uint16_t* a_src[2];
-  const uint16_t* b_src[2];
+  // ---- load side.  A instruction i (0..3) of wave w fills rows 8*(4w+i) ..
+  // +7 (lane/8 picks the row, lane%8 the chunk position); it is issued only if
+  // its first row lies inside the tile (rows past the end inside a partly
+  // valid group repeat the tile's last row).  B instruction i fills k-rows
+  // 2*(4w+i) + lane/32, chunk position lane%32; columns past N read column 0.
+  // Every load is in bounds, and what the clamped ones bring only reaches
+  // outputs that are never stored.
+  const uint16_t* a_src[GB_A_LOADS];
+  const uint16_t* b_src[GB_B_LOADS];
+  int a_groups = 0;  // A instructions of this wave that are issued (a prefix of i)
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 16 * (2 * w + i) + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
+  for (int i = 0; i < GB_A_LOADS; ++i) {
+    const int r = 8 * (4 * w + i) + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int64_t prow = seg + m0 + min(r, rows - 1);
     const int64_t arow = p.a_gather ? (int64_t)p.a_gather[prow] : prow;
     a_src[i] = p.A + arow * p.lda + c * 8;
-
-    const int k = 2 * (2 * w + i) + (lane >> 5);
+    a_groups += 8 * (4 * w + i) < rows ? 1 : 0;
+  }
+  a_groups = __builtin_amdgcn_readfirstlane(a_groups);
+#pragma unroll
+  for (int i = 0; i < GB_B_LOADS; ++i) {
+    const int k = 2 * (4 * w + i) + (lane >> 5);
     const int cb = (lane & 31) ^ (4 * (k & 3));
     int gcol;
     if (EPI == kEpiSwiGLU) {
@@ -398,15 +292,18 @@ __global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p)
     b_src[i] = p.Bg + (int64_t)e * p.b_stride + (int64_t)k * p.ldb + gcol;
   }
   const int64_t b_kstep = (int64_t)GB_K * p.ldb;
-  auto issue = [&](uint16_t* stage, int kt) __attribute__((always_inline)) {
+  auto issue_a = [&](uint16_t* dst, int kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      __builtin_amdgcn_global_load_lds(a_src[i] + kt * GB_K,
-                                       (lds_void_t*)(stage + (2 * w + i) * 512), 16, 0, 0);
+    for (int i = 0; i < GB_A_LOADS; ++i)
+      if (i < a_groups)
+        __builtin_amdgcn_global_load_lds(a_src[i] + kt * GB_K,
+                                         (lds_void_t*)(dst + (4 * w + i) * 512), 16, 0, 0);
+  };
+  auto issue_b = [&](uint16_t* dst, int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < GB_B_LOADS; ++i)
       __builtin_amdgcn_global_load_lds(b_src[i] + kt * b_kstep,
-                                       (lds_void_t*)(stage + GB_A_ELEMS + (2 * w + i) * 512), 16,
-                                       0, 0);
-    }
+                                       (lds_void_t*)(dst + (4 * w + i) * 512), 16, 0, 0);
   };
 
   // ---- compute side
@@ -421,48 +318,43 @@ __global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p)
 #pragma unroll
     for (int f = 0; f < 2; ++f) acc[j][f] = f32x16_t{};
 
-  // per-lane LDS element offsets inside a stage (the same for every stage)
-  int a_off[4][2];  // [sub-tile][k-substep of 16]
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int r = 32 * (wm + 2 * j) + (lane & 31);
-      const int c = 2 * ks + (lane >> 5);
-      a_off[j][ks] = r * GB_K + ((c ^ ((r >> 2) & 3)) * 8);
-    }
+  // per-lane LDS element offsets inside a slot (the same for every step)
+  const int arow_l = wm * 32 + (lane & 31);  // row inside sub-tile 0 of this wave
+  const int a_sw = (arow_l >> 1) & 7;        // (r >> 1) & 7 is the same for r + 64 j
+  const int a_base = arow_l * GB_K;
   // B fragment of column group f, k-substep ks: two transposing reads, the second
   // 4 k-rows further on (same swizzle, since (k + 4) & 3 == k & 3).
-  int b_off[2][2];
+  int b_off[2][4];
   {
     const int G = lane >> 4, j4 = (lane & 15) >> 2, q = lane & 3;
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < 4; ++ks) {
         const int k = ks * 16 + 8 * (G >> 1) + j4;
         const int c = bcol(f) / 8 + 2 * (G & 1) + (q >> 1);
-        b_off[f][ks] = GB_A_ELEMS + k * GB_N + ((c ^ (4 * (k & 3))) * 8) + (q & 1) * 4;
+        b_off[f][ks] = k * GB_N + ((c ^ (4 * (k & 3))) * 8) + (q & 1) * 4;
       }
   }
 
-  auto compute = [&](const uint16_t* stage) __attribute__((always_inline)) {
+  auto compute = [&](const uint16_t* as, const uint16_t* bs) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < GB_K / 16; ++ks) {
       bf16x8_t bf[2];
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
-        const uint16_t* bp = stage + b_off[f][ks];
+        const uint16_t* bp = bs + b_off[f][ks];
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)bp);
         const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(bp + 4 * GB_N));
         typedef short s16x8_t __attribute__((ext_vector_type(8)));
         const s16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         bf[f] = __builtin_bit_cast(bf16x8_t, v);
       }
+      const int a_chunk = ((2 * ks + (lane >> 5)) ^ a_sw) * 8;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (!sub_ok[j]) continue;
-        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(stage + a_off[j][ks]);
+        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(as + a_base + j * 64 * GB_K + a_chunk);
 #pragma unroll
         for (int f = 0; f < 2; ++f)
           acc[j][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[f], acc[j][f], 0, 0, 0);
@@ -470,39 +362,43 @@ __global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p)
     }
   };
 
-  // Step t: wait for this wave's loads of stage t (the 3 later stages may stay
-  // in flight), barrier (every wave's stage-t data has landed and every wave is
-  // done with the slot of stage t-1), refill that slot with stage t+4, multiply
-  // stage t.  Stages past the end are requested too (as copies of the last one)
-  // so that every step has the same number of loads in flight; they land in
-  // slots that are never read again.
-  auto step = [&](const uint16_t* cur, uint16_t* refill, int t) __attribute__((always_inline)) {
+  // Step t: wait until only this wave's B loads of step t+1 are outstanding
+  // (A of step t, issued before them, and B of step t, issued earlier, have
+  // landed), barrier (every wave's data of step t has landed and every wave is
+  // done with the slots of step t-1), refill those slots with A of step t+1 and
+  // B of step t+2, multiply step t.  Steps past the end are requested too (as
+  // copies of the last one) so that the count of loads in flight is the same
+  // at every step; they land in slots that are never read again.
+  auto step = [&](const uint16_t* a_cur, uint16_t* a_next, const uint16_t* b_cur, uint16_t* b_next,
+                  int t) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((GB_STAGES - 2) * GB_LOADS_PER_STAGE));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(GB_B_LOADS));
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    issue(refill, min(t + GB_STAGES - 1, nkt - 1));
-    compute(cur);
+    issue_a(a_next, min(t + 1, nkt - 1));
+    issue_b(b_next, min(t + 2, nkt - 1));
+    compute(a_cur, b_cur);
   };
 
-  issue(st0, 0);
-  issue(st1, min(1, nkt - 1));
-  issue(st2, min(2, nkt - 1));
-  issue(st3, min(3, nkt - 1));
+  issue_b(sb0, 0);
+  issue_a(sa0, 0);
+  issue_b(sb1, min(1, nkt - 1));
   int t = 0;
-  for (; t + GB_STAGES <= nkt; t += GB_STAGES) {
-    step(st0, st4, t);
-    step(st1, st0, t + 1);
-    step(st2, st1, t + 2);
-    step(st3, st2, t + 3);
-    step(st4, st3, t + 4);
+  for (; t + 6 <= nkt; t += 6) {
+    step(sa0, sa1, sb0, sb2, t);
+    step(sa1, sa0, sb1, sb0, t + 1);
+    step(sa0, sa1, sb2, sb1, t + 2);
+    step(sa1, sa0, sb0, sb2, t + 3);
+    step(sa0, sa1, sb1, sb0, t + 4);
+    step(sa1, sa0, sb2, sb1, t + 5);
   }
-  if (t < nkt) step(st0, st4, t);
-  if (t + 1 < nkt) step(st1, st0, t + 1);
-  if (t + 2 < nkt) step(st2, st1, t + 2);
-  if (t + 3 < nkt) step(st3, st2, t + 3);
+  if (t < nkt) step(sa0, sa1, sb0, sb2, t);
+  if (t + 1 < nkt) step(sa1, sa0, sb1, sb0, t + 1);
+  if (t + 2 < nkt) step(sa0, sa1, sb2, sb1, t + 2);
+  if (t + 3 < nkt) step(sa1, sa0, sb0, sb2, t + 3);
+  if (t + 4 < nkt) step(sa0, sa1, sb1, sb0, t + 4);
   // no load may still be writing LDS when the block ends
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
@@ -545,7 +441,7 @@ hipError_t launch_mfma_nt(const NtArgs& a, hipStream_t s) {
   p.kt_per_split = a.k_tiles_per_split;
   p.C = a.out;
   dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, a.splits);
-  mfma_kernel<false, kEpiPartialF32><<<grid, 256, 0, s>>>(p);
+  mfma_nt_kernel<<<grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
