@@ -183,6 +183,39 @@ def cpu_baseline(cfg, tin, small, seconds):
                       "+ shared, combine), %.1f s" % (done, cfg.T, cfg.name, cfg.k, spent)}
 
 
+def measure_norms(launches):
+    """Standalone RMSNorm entry point at the widths of the block's other norms: HBM
+    roofline of each (algorithmic bytes = rows*width read + rows*width written + the
+    gain, in bf16), timed with HIP events over `launches` calls on the current stream."""
+    import torch
+    import workloads
+    import mixture_experts_transformer_rmsnorm_amd as moe
+    out = {}
+    g = torch.Generator(device="cuda")
+    for name, c in workloads.NORM_CASES.items():
+        g.manual_seed(1234)
+        x = torch.randn((c.rows, c.stride), generator=g, device="cuda").to(torch.bfloat16)
+        w = (1.0 + 0.1 * torch.randn((c.width,), generator=g, device="cuda")).to(torch.bfloat16)
+        o = torch.empty_like(x)
+        for _ in range(3):
+            moe.moe_rmsnorm(None, moe.MOE_DTYPE_BF16, c.rows, c.width, c.eps, x, c.stride, w, o, c.stride)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(launches):
+            moe.moe_rmsnorm(None, moe.MOE_DTYPE_BF16, c.rows, c.width, c.eps, x, c.stride, w, o, c.stride)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        nbytes = 2 * c.rows * c.width * 2 + c.width * 2
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"rows": c.rows, "width": c.width, "row_stride": c.stride, "ms": round(ms, 4),
+                     "algorithmic_bytes": nbytes, "GB_per_s": round(gbs, 1),
+                     "frac_of_hbm_peak": round(gbs / 8000.0, 4)}
+        log("rmsnorm %s: %d x %d, %.4f ms, %.1f GB/s" % (name, c.rows, c.width, ms, gbs))
+        del x, w, o
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +226,11 @@ def main():
                     help="second workload of the same shape family reported in the line ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--extras", default="norms",
+                    help="comma list of extra entry points measured into the line's 'extras' "
+                         "('norms'; '' = none)")
+    ap.add_argument("--only-extras", action="store_true",
+                    help="measure only the extras and print them as one JSON line (profiling)")
     ap.add_argument("--calib-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "kernel for scaling hardware byte counters)")
@@ -215,6 +253,17 @@ def main():
         torch.cuda.synchronize()
         log("calibration copy: %d bytes read, %d bytes written" % (n, n))
         del src, dst
+    extras_req = [e for e in args.extras.split(",") if e]
+
+    def run_extras():
+        ext = {}
+        if "norms" in extras_req:
+            ext["rmsnorm"] = measure_norms(max(args.steps // 2, 5))
+        return ext
+
+    if args.only_extras:
+        print(json.dumps({"extras": run_extras()}), flush=True)
+        return
     cfg = workloads.config(args.config)
     log("drawing %s inputs on the device" % cfg.name)
     tin = workloads.make_torch(cfg, 0, device="cuda", weights="device")
@@ -259,6 +308,8 @@ def main():
                                  "roofline": r2["roofline"], "step_roofline": r2["step_roofline"],
                                  "stage_ms": r2["stage_ms"]}
             del tin2
+    if extras_req:
+        line["extras"] = run_extras()
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, tin, small, args.cpu_seconds)
     print(json.dumps(line), flush=True)

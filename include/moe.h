@@ -138,6 +138,33 @@ MOE_API moe_status_t moe_read_routing(moe_plan_t plan, const void* workspace, vo
                               int64_t num_tokens, int32_t top_k, int32_t* topk_idx, float* topk_w,
                               int32_t* counts);
 
+/* Standalone RMSNorm, the same operation as the sublayer's first step, for the
+ * block's other norms ("GLM-5 · Input features", excerpt rmsnorm: fp32
+ * normalisation by the root mean square over the last dimension, cast back to
+ * the input dtype, then the per-feature gain; excerpt block: the norm in front
+ * of attention, width dim; "GLM-5 · MoE transformer block", Parameters: the MLA
+ * latent norms, query latent width 2048, and the per-head query/key norms):
+ *
+ *   out[r, i] = D(weight[i] * D(x[r, i] * rsqrt(mean_i x[r, i]^2 + eps)))
+ *
+ * for r < rows, i < width.  x row r starts at x + r * x_stride elements, out
+ * row r at out + r * out_stride (strides in elements, >= width), so a norm over
+ * the leading columns of a wider row (a latent that shares its row with other
+ * features) needs no copy.  Per-head norms pass rows = tokens * heads and
+ * width = the head dimension.
+ *  dtype     moe_dtype_t of x, weight and out (D).
+ *  width     a multiple of 16 / sizeof(D) (8 for bf16, 4 for fp32), <= 2^24.
+ *  strides   multiples of 16 / sizeof(D); pointers 16-byte aligned device memory.
+ *  weight    [width] D.
+ *  eps       > 0 and finite.
+ * out may be x itself (same stride); any other overlap is INVALID_VALUE.
+ * rows == 0 is a successful no-op that reads no pointer.  Enqueued on `stream`
+ * (a hipStream_t; NULL = default stream); returns asynchronously; the caller
+ * owns every buffer. */
+MOE_API moe_status_t moe_rmsnorm(void* stream, int32_t dtype, int64_t rows, int32_t width, float eps,
+                                 const void* x, int64_t x_stride, const void* weight, void* out,
+                                 int64_t out_stride);
+
 /* Intermediate buffers of the last forward call (tests, diagnostics). */
 typedef enum {
   MOE_BUF_H = 0,          /* [T, d] D: normalised input */

@@ -35,7 +35,8 @@ ABI_VERSION = 1
 
 EXPORTS = ("moe_plan_create", "moe_plan_destroy", "moe_block_forward", "moe_read_routing",
            "moe_read_buffer", "moe_buffer_bytes", "moe_plan_path", "moe_set_stage_timing",
-           "moe_stage_times", "moe_stage_name", "moe_status_string", "moe_abi_version")
+           "moe_stage_times", "moe_stage_name", "moe_status_string", "moe_abi_version",
+           "moe_rmsnorm")
 
 
 class MoEError(RuntimeError):
@@ -88,10 +89,11 @@ def load(path: str = LIB_PATH):
         lib.moe_stage_name.restype = ctypes.c_char_p
         lib.moe_status_string.argtypes = [i32]
         lib.moe_status_string.restype = ctypes.c_char_p
+        lib.moe_rmsnorm.argtypes = [P, i32, i64, i32, ctypes.c_float, P, i64, P, P, i64]
         lib.moe_abi_version.argtypes = []
         lib.moe_abi_version.restype = i32
         for fn in ("moe_plan_create", "moe_plan_destroy", "moe_block_forward", "moe_read_routing",
-                   "moe_read_buffer", "moe_set_stage_timing", "moe_stage_times"):
+                   "moe_read_buffer", "moe_set_stage_timing", "moe_stage_times", "moe_rmsnorm"):
             getattr(lib, fn).restype = i32
         if lib.moe_abi_version() != ABI_VERSION:
             raise ImportError("libmoe_mi355x.so ABI %d != binding ABI %d"
@@ -166,6 +168,31 @@ def moe_block_forward(plan, workspace, workspace_bytes, stream, num_tokens, x, n
         _ptr(norm_w), _ptr(router_w), _ptr(corr_bias), _ptr(gate_up), _ptr(down),
         _ptr(shared_gate), _ptr(shared_up), _ptr(shared_down), top_k, routed_scale, _ptr(out)),
         "moe_block_forward")
+
+
+def moe_rmsnorm(stream, dtype, rows, width, eps, x, x_stride, weight, out, out_stride) -> None:
+    _check(load().moe_rmsnorm(_stream(stream), dtype, rows, width, eps, _ptr(x), x_stride,
+                              _ptr(weight), _ptr(out), out_stride), "moe_rmsnorm")
+
+
+def rmsnorm(x, weight, eps=1e-6, out=None, stream=None):
+    """RMSNorm over the last dimension of x ([..., width] or a 2-D view whose rows
+    are strided, e.g. the leading columns of wider rows); returns out (new, or the
+    given tensor, which may be x itself)."""
+    import torch
+    width = x.shape[-1]
+    x2 = x.reshape(-1, width) if x.dim() != 2 else x
+    if x2.stride(-1) != 1:
+        raise ValueError("rmsnorm: the last dimension must be contiguous")
+    if out is None:
+        out = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    o2 = out.reshape(-1, width) if out.dim() != 2 else out
+    if o2.stride(-1) != 1 or o2.shape != x2.shape:
+        raise ValueError("rmsnorm: out must match x with a contiguous last dimension")
+    dt = {torch.bfloat16: MOE_DTYPE_BF16, torch.float32: MOE_DTYPE_F32}[x.dtype]
+    moe_rmsnorm(stream, dt, x2.shape[0], width, eps, x2, x2.stride(0) if x2.shape[0] > 1 else width,
+                weight, o2, o2.stride(0) if o2.shape[0] > 1 else width)
+    return out
 
 
 def moe_read_routing(plan, workspace, stream, num_tokens, top_k, topk_idx=None, topk_w=None,

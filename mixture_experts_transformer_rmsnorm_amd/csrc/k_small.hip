@@ -4,6 +4,8 @@
 // SwiGLU finalisation and the weighted combine with the residual.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -12,56 +14,144 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // RMSNorm ("GLM-5 · Input features", excerpt rmsnorm: fp32 normalisation by the
 // root mean square over the feature dimension, no centring, cast back to the
-// input dtype, then the per-feature gain).  One 256-thread block per row.
-// The mean of squares is accumulated in fp64 and rounded once to fp32; sqrt
-// and the reciprocal are evaluated in fp64 and rounded once, which gives
-// exactly the IEEE fp32 sqrt and divide.
-template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x,
-                                                      const T* __restrict__ w, T* __restrict__ h,
-                                                      int d, float eps) {
-  constexpr int V = Elem<T>::kVec;
-  const int64_t row = blockIdx.x;
-  const T* xr = x + row * d;
-  const int nvec = d / V;
-  double ss = 0.0;
-  for (int i = threadIdx.x; i < nvec; i += blockDim.x) {
-    float f[V];
-    Elem<T>::unpack(ldg16(xr + (int64_t)i * V), f);
-#pragma unroll
-    for (int q = 0; q < V; ++q) ss += (double)f[q] * (double)f[q];
-  }
-  ss = wave_sum(ss);
-  __shared__ double red[4];
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  if (lane == 0) red[wid] = ss;
-  __syncthreads();
-  const double tot = red[0] + red[1] + red[2] + red[3];
-  const float ms = (float)(tot / (double)d);
-  const float den = ms + eps;
-  const float sq = (float)sqrt((double)den);
-  const float r = (float)(1.0 / (double)sq);
-  T* hr = h + row * d;
-  for (int i = threadIdx.x; i < nvec; i += blockDim.x) {
-    float f[V], g[V];
-    Elem<T>::unpack(ldg16(xr + (int64_t)i * V), f);
-    Elem<T>::unpack(ldg16(w + (int64_t)i * V), g);
-#pragma unroll
-    for (int q = 0; q < V; ++q) f[q] = Elem<T>::round(g[q] * Elem<T>::round(f[q] * r));
-    stg16(hr + (int64_t)i * V, Elem<T>::pack(f));
-  }
+// input dtype, then the per-feature gain).  The mean of squares is accumulated
+// in fp64 and rounded once to fp32; sqrt and the reciprocal are evaluated in
+// fp64 and rounded once, which gives exactly the IEEE fp32 sqrt and divide.
+// Rows are `ldx` / `ldh` elements apart; each element of a row is read before
+// the same thread writes it, so h may alias x.
+
+__device__ __forceinline__ float rms_scale(double sum_sq, int d, float eps) {
+  const float ms = (float)(sum_sq / (double)d);
+  const float sq = (float)sqrt((double)(ms + eps));
+  return (float)(1.0 / (double)sq);
 }
 
-hipError_t launch_rmsnorm(int dtype, const void* x, const void* w, void* h, int64_t T, int d,
-                          float eps, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  if (dtype == kBF16)
-    rmsnorm_kernel<bf16><<<dim3((unsigned)T), 256, 0, s>>>((const bf16*)x, (const bf16*)w,
-                                                           (bf16*)h, d, eps);
+template <typename T>
+__device__ __forceinline__ double sum_sq(const uint4& v) {
+  constexpr int V = Elem<T>::kVec;
+  float f[V];
+  Elem<T>::unpack(v, f);
+  double ss = 0.0;
+#pragma unroll
+  for (int q = 0; q < V; ++q) ss += (double)f[q] * (double)f[q];
+  return ss;
+}
+
+template <typename T>
+__device__ __forceinline__ uint4 rms_vec(const uint4& xv, const T* w, int i, float r) {
+  constexpr int V = Elem<T>::kVec;
+  float f[V], g[V];
+  Elem<T>::unpack(xv, f);
+  Elem<T>::unpack(ldg16(w + (int64_t)i * V), g);
+#pragma unroll
+  for (int q = 0; q < V; ++q) f[q] = Elem<T>::round(g[q] * Elem<T>::round(f[q] * r));
+  return Elem<T>::pack(f);
+}
+
+// One row handled by `step` threads starting at vector i0.  The first NV vectors of
+// each thread stay in registers between the sum of squares and the scaling, so a
+// row of up to NV * step vectors is read from memory once; longer rows read the
+// rest again.  The partial sum of squares goes through `reduce`.
+template <typename T, int NV, typename Reduce>
+__device__ __forceinline__ void rms_row(const T* xr, const T* w, T* hr, int nvec, int i0, int step,
+                                        int d, float eps, Reduce reduce) {
+  constexpr int V = Elem<T>::kVec;
+  uint4 xv[NV];
+  double ss = 0.0;
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int i = i0 + u * step;
+    if (i < nvec) {
+      xv[u] = ldg16(xr + (int64_t)i * V);
+      ss += sum_sq<T>(xv[u]);
+    }
+  }
+  for (int i = i0 + NV * step; i < nvec; i += step) ss += sum_sq<T>(ldg16(xr + (int64_t)i * V));
+  const float r = rms_scale(reduce(ss), d, eps);
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int i = i0 + u * step;
+    if (i < nvec) stg16(hr + (int64_t)i * V, rms_vec(xv[u], w, i, r));
+  }
+  for (int i = i0 + NV * step; i < nvec; i += step)
+    stg16(hr + (int64_t)i * V, rms_vec(ldg16(xr + (int64_t)i * V), w, i, r));
+}
+
+// Wide rows: one 256-thread block per row (rows of up to 4 * 256 vectors are read once).
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, int64_t ldx, const T* __restrict__ w,
+                                                      T* h, int64_t ldh, int d, float eps) {
+  constexpr int V = Elem<T>::kVec;
+  const int64_t row = blockIdx.x;
+  __shared__ double red[4];
+  auto reduce = [&](double ss) {
+    ss = wave_sum(ss);
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    if (lane == 0) red[wid] = ss;
+    __syncthreads();
+    return red[0] + red[1] + red[2] + red[3];
+  };
+  rms_row<T, 4>(x + row * ldx, w, h + row * ldh, d / V, threadIdx.x, 256, d, eps, reduce);
+}
+
+// Narrower rows (the latent and per-head norms): LPR lanes per row, 256 / LPR
+// rows per block, up to NV vectors per lane held in registers; the row's partial
+// sums are combined by shuffles inside its lanes.
+template <typename T, int LPR, int NV>
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const T* x, int64_t ldx,
+                                                           const T* __restrict__ w, T* h,
+                                                           int64_t ldh, int64_t rows, int d,
+                                                           float eps) {
+  constexpr int V = Elem<T>::kVec;
+  const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  if (row >= rows) return;  // whole lane groups leave together; no block barrier follows
+  auto reduce = [](double ss) {
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+    return ss;
+  };
+  rms_row<T, NV>(x + row * ldx, w, h + row * ldh, d / V, threadIdx.x % LPR, LPR, d, eps, reduce);
+}
+
+template <typename T>
+static hipError_t launch_rmsnorm_t(const void* x, int64_t ldx, const void* w, void* h, int64_t ldh,
+                                   int64_t T_, int d, float eps, hipStream_t s) {
+  constexpr int V = Elem<T>::kVec;
+  const int nvec = d / V;
+  const T* xp = (const T*)x;
+  const T* wp = (const T*)w;
+  T* hp = (T*)h;
+  auto rows_launch = [&](auto lpr_tag, auto nv_tag) {
+    constexpr int LPR = decltype(lpr_tag)::value, NV = decltype(nv_tag)::value;
+    const int64_t blocks = (T_ + 256 / LPR - 1) / (256 / LPR);
+    rmsnorm_rows_kernel<T, LPR, NV><<<dim3((unsigned)blocks), 256, 0, s>>>(xp, ldx, wp, hp, ldh, T_,
+                                                                         d, eps);
+  };
+  using I64 = std::integral_constant<int, 64>;
+  if (nvec >= 512)
+    rmsnorm_kernel<T><<<dim3((unsigned)T_), 256, 0, s>>>(xp, ldx, wp, hp, ldh, d, eps);
+  else if (nvec >= 256)
+    rows_launch(I64{}, std::integral_constant<int, 8>{});
+  else if (nvec >= 128)
+    rows_launch(I64{}, std::integral_constant<int, 4>{});
+  else if (nvec >= 64)
+    rows_launch(I64{}, std::integral_constant<int, 2>{});
+  else if (nvec >= 32)
+    rows_launch(std::integral_constant<int, 32>{}, std::integral_constant<int, 2>{});
+  else if (nvec >= 16)
+    rows_launch(std::integral_constant<int, 16>{}, std::integral_constant<int, 2>{});
+  else if (nvec >= 8)
+    rows_launch(std::integral_constant<int, 8>{}, std::integral_constant<int, 2>{});
   else
-    rmsnorm_kernel<float><<<dim3((unsigned)T), 256, 0, s>>>((const float*)x, (const float*)w,
-                                                            (float*)h, d, eps);
+    rows_launch(std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{});
   return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(int dtype, const void* x, int64_t ldx, const void* w, void* h,
+                          int64_t ldh, int64_t T, int d, float eps, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (dtype == kBF16) return launch_rmsnorm_t<bf16>(x, ldx, w, h, ldh, T, d, eps, s);
+  return launch_rmsnorm_t<float>(x, ldx, w, h, ldh, T, d, eps, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -30,8 +30,9 @@ struct RouteHeader {
 };
 
 // ---------------------------------------------------------------- small kernels
-hipError_t launch_rmsnorm(int dtype, const void* x, const void* w, void* h, int64_t T, int d,
-                          float eps, hipStream_t s);
+// h[t] = RMSNorm(x[t]) * w for T rows of d features; rows ldx / ldh elements apart.
+hipError_t launch_rmsnorm(int dtype, const void* x, int64_t ldx, const void* w, void* h,
+                          int64_t ldh, int64_t T, int d, float eps, hipStream_t s);
 
 // out_part[z][m][n] = sum_{k in split z} A[m][k] * B[n][k]; B row n is
 // B1 + n*ldb for n < n_split, else B2 + (n - n_split)*ldb.  fp32 results.

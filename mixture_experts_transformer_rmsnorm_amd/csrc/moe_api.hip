@@ -364,7 +364,7 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   const Split sgsplit =
       has_shared ? nt_split(T, 2 * (int64_t)Is, d, tm, tn, tk, kMaxSharedSplits) : Split{0, 0};
 
-  stage(kStNorm, [&] { return launch_rmsnorm(dt, x, norm_w, h, T, d, c.eps, s); });
+  stage(kStNorm, [&] { return launch_rmsnorm(dt, x, d, norm_w, h, d, T, d, c.eps, s); });
   stage(kStRouter,
         [&] { return nt(h, d, router_w, router_w, d, E, logits, E, d, kMaxRouterSplits); });
   stage(kStTopk, [&] {
@@ -421,6 +421,29 @@ size_t moe_buffer_bytes(moe_plan_t p, int64_t T, int32_t k, int32_t which) {
     case MOE_BUF_SHARED_ACT: return (size_t)T * c.shared_inter * p->es;
   }
   return 0;
+}
+
+moe_status_t moe_rmsnorm(void* stream, int32_t dtype, int64_t rows, int32_t width, float eps,
+                         const void* x, int64_t x_stride, const void* weight, void* out,
+                         int64_t out_stride) {
+  if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16) return MOE_ERROR_NOT_SUPPORTED;
+  const int64_t es = dtype == MOE_DTYPE_BF16 ? 2 : 4, vec = 16 / es;
+  if (rows < 0 || rows > INT32_MAX || width <= 0 || width > (1 << 24) || width % vec ||
+      x_stride < width || out_stride < width || x_stride % vec || out_stride % vec ||
+      !(eps > 0.0f) || !isfinite(eps))
+    return MOE_ERROR_INVALID_VALUE;
+  if (rows == 0) return MOE_SUCCESS;
+  if (!x || !weight || !out) return MOE_ERROR_INVALID_VALUE;
+  if (misaligned(x) || misaligned(weight) || misaligned(out)) return MOE_ERROR_MISALIGNED;
+  // out may be x itself (same stride); any other overlap of the two row ranges is rejected
+  const uintptr_t x0 = (uintptr_t)x, x1 = x0 + (uintptr_t)(((rows - 1) * x_stride + width) * es);
+  const uintptr_t o0 = (uintptr_t)out, o1 = o0 + (uintptr_t)(((rows - 1) * out_stride + width) * es);
+  const bool overlap = x0 < o1 && o0 < x1;
+  if (overlap && !(x0 == o0 && x_stride == out_stride)) return MOE_ERROR_INVALID_VALUE;
+  const hipError_t e = moe::launch_rmsnorm(dtype == MOE_DTYPE_BF16 ? moe::kBF16 : moe::kF32, x,
+                                           x_stride, weight, out, out_stride, rows, width, eps,
+                                           (hipStream_t)stream);
+  return e == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
 }
 
 moe_status_t moe_read_buffer(moe_plan_t p, const void* workspace, void* stream, int64_t T,

@@ -141,3 +141,34 @@ def test_reader_validation():
             moe.moe_read_routing(plan, FAKE, 0, 65, 8)
     finally:
         moe.moe_plan_destroy(plan)
+
+
+# moe_rmsnorm: every case below is rejected (or is the rows == 0 no-op) before any
+# device work, so fake, never dereferenced addresses are enough.
+_X, _W, _O = 0x100000, 0x200000, 0x300000
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3), moe.MOE_ERROR_NOT_SUPPORTED),
+    (dict(rows=-1), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(width=0), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(width=100), moe.MOE_ERROR_INVALID_VALUE),            # bf16 rows need multiples of 8
+    (dict(x_stride=64), moe.MOE_ERROR_INVALID_VALUE),          # stride below width
+    (dict(out_stride=132), moe.MOE_ERROR_INVALID_VALUE),       # not a multiple of 8
+    (dict(eps=0.0), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(eps=float("inf")), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(x=None), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(weight=None), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(out=_O + 2), moe.MOE_ERROR_MISALIGNED),
+    (dict(out=_X + 16), moe.MOE_ERROR_INVALID_VALUE),          # overlaps x, not x itself
+    (dict(out=_X, out_stride=136), moe.MOE_ERROR_INVALID_VALUE),  # in place needs equal strides
+    (dict(rows=0, x=None, weight=None, out=None), moe.MOE_SUCCESS),
+])
+def test_rmsnorm_validation(kw, status):
+    args = dict(dtype=moe.MOE_DTYPE_BF16, rows=4, width=128, eps=1e-6, x=_X, x_stride=128,
+                weight=_W, out=_O, out_stride=128)
+    args.update(kw)
+    got = moe.load().moe_rmsnorm(0, args["dtype"], args["rows"], args["width"], args["eps"],
+                                 args["x"], args["x_stride"], args["weight"], args["out"],
+                                 args["out_stride"])
+    assert got == status

@@ -12,7 +12,8 @@ shared expert as nn.Linear [out, in] weights).
 Random streams: NumPy ``Generator(PCG64)`` seeded by ``SeedSequence(seed,
 spawn_key=(tensor_id, ...))``.  Tensor ids: x 0, norm_w 1, router_w 2,
 corr_bias 3, gate_up 4, down 5, shared_gate 6, shared_up 7, shared_down 8,
-zipf rank permutation 9, row redraws 10.  Values are drawn in fp32 and rounded
+zipf rank permutation 9, row redraws 10; standalone RMSNorm inputs 11 (x), 12
+(per-feature scales), 13 (gain).  Values are drawn in fp32 and rounded
 to bfloat16 (round to nearest even) for bf16 workloads.
 
 Expert weights of the GLM-5-sized workloads (19.4 GB in bf16) can instead be
@@ -31,6 +32,7 @@ import numpy as np
 
 TID_X, TID_NORM, TID_ROUTER, TID_BIAS, TID_GATE_UP, TID_DOWN = 0, 1, 2, 3, 4, 5
 TID_SH_GATE, TID_SH_UP, TID_SH_DOWN, TID_ZIPF, TID_REDRAW = 6, 7, 8, 9, 10
+TID_NORM_X, TID_NORM_SCALE, TID_NORM_GAIN = 11, 12, 13
 
 # Strength of the Zipf-shaped correction bias of the skewed workload.  Written by
 # tests/golden/calibrate_zipf.py (output tests/golden/zipf_beta.json): the value
@@ -270,3 +272,44 @@ def weight_bytes(cfg: MoEConfig) -> int:
 def param_count(cfg: MoEConfig) -> int:
     """Learned parameters of the MoE sublayer plus the router's correction-bias buffer."""
     return cfg.E * 3 * cfg.d * cfg.I + 3 * cfg.d * cfg.Is + cfg.E * cfg.d + cfg.E
+
+
+# ----------------------------------------------------------------------------- RMSNorm cases
+@dataclasses.dataclass(frozen=True)
+class NormCase:
+    """A standalone RMSNorm of the block: rows x width, rows `stride` elements apart."""
+    name: str
+    rows: int
+    width: int
+    stride: int
+    dtype: str = "bf16"
+    eps: float = 1e-6
+    note: str = ""
+
+
+# The widths of the block's other norms.  The input norm runs at the hidden size and
+# the query-latent norm at 2048 ("GLM-5 · Query latent": q latent 2048; "GLM-5 ·
+# Input features", excerpt block).  The key-value latent width is not printed: 512
+# latent features in rows of 576 (with 64 rotary features after them) is synthetic.
+# The per-head query/key norm runs over the query-key head width, 256 (the softmax
+# scale printed on "GLM-5 · Query latent" is 1/sqrt(256)); rows = tokens x heads,
+# with 64 heads as a synthetic head count.
+NORM_CASES = {
+    "input_norm": NormCase("input_norm", 4096, 6144, 6144, note="hidden size"),
+    "q_latent_norm": NormCase("q_latent_norm", 4096, 2048, 2048, note="query latent"),
+    "kv_latent_norm": NormCase("kv_latent_norm", 4096, 512, 576,
+                               note="key-value latent (synthetic width), strided rows"),
+    "qk_head_norm": NormCase("qk_head_norm", 4096 * 64, 256, 256,
+                             note="per-head query/key norm (synthetic head count)"),
+}
+
+
+def draw_norm(rows: int, width: int, stride: int, dtype: str, seed: int = 0):
+    """x [rows, stride] (only the first `width` columns are the norm's input; the rest
+    is filler that must come through untouched) and gain [width], storage dtype.
+    x = N(0, 1) times a per-feature log-normal scale (activations with uneven feature
+    magnitudes); gain = 1 + 0.1 N(0, 1)."""
+    scale = np.exp(0.5 * _rng(seed, TID_NORM_SCALE).standard_normal(stride)).astype(np.float32)
+    x = _rng(seed, TID_NORM_X).standard_normal((rows, stride), dtype=np.float32) * scale
+    gain = (1.0 + 0.1 * _rng(seed, TID_NORM_GAIN).standard_normal(width)).astype(np.float32)
+    return _store(x, dtype), _store(gain, dtype)
