@@ -58,9 +58,10 @@ def _load():
             lib.oracle_counts.argtypes = [i64, i32, i32, P, P, P]
             lib.oracle_experts.argtypes = [i64, P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P,
                                            P, P, P, P, P, P, P, P, P]
+            lib.oracle_dense_mlp.argtypes = [i64, i32, i32, i32, P, P, P, P, P, P, P, P]
             lib.oracle_num_threads.argtypes = []
             for fn in ("oracle_num_threads", "oracle_round_to_dtype", "oracle_rmsnorm", "oracle_router_scores",
-                       "oracle_select", "oracle_counts", "oracle_experts"):
+                       "oracle_select", "oracle_counts", "oracle_experts", "oracle_dense_mlp"):
                 getattr(lib, fn).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -219,3 +220,33 @@ def forward(inp, tokens=None, debug=False):
         r["delta"], r["out"] = res
     r["counts"], r["offsets"] = counts(r["idx"], len(inp["gate_up"]))
     return r
+
+
+def dense_mlp(x, h, gate, up, down, dtype, debug=False):
+    """Step O9: dense SwiGLU MLP block on h (the RMSNorm of x): returns (delta fp64 [T, d],
+    out [T, d] float32 holding D values[, act fp64 [T, Id]])."""
+    x = _storage(x, dtype)
+    h = np.ascontiguousarray(h, np.float32)
+    gate, up, down = (_storage(a, dtype) for a in (gate, up, down))
+    T, d = x.shape
+    Id = gate.shape[0]
+    if gate.shape != (Id, d) or up.shape != (Id, d) or down.shape != (d, Id) or h.shape != (T, d):
+        raise ValueError("dense_mlp: shapes x %s h %s gate %s up %s down %s" % (
+            x.shape, h.shape, gate.shape, up.shape, down.shape))
+    delta = np.empty((T, d), np.float64)
+    out = np.empty((T, d), np.float32)
+    act = np.empty((T, Id), np.float64) if debug else None
+    _check(_load().oracle_dense_mlp(T, d, Id, dtype, _ptr(x), _ptr(h), _ptr(gate), _ptr(up),
+                                    _ptr(down), _ptr(delta), _ptr(out), _ptr(act)), "dense_mlp")
+    return (delta, out, act) if debug else (delta, out)
+
+
+def dense_block(x, norm_w, gate, up, down, dtype, eps=1e-6, debug=False):
+    """Steps O1 + O9: out = x + mlp(rmsnorm(x)) for a dense block; returns a dict with
+    h, delta, out (and act when debug)."""
+    h = rmsnorm(x, norm_w, dtype, eps)
+    r = dense_mlp(x, h, gate, up, down, dtype, debug)
+    res = dict(h=h, delta=r[0], out=r[1])
+    if debug:
+        res["act"] = r[2]
+    return res

@@ -352,3 +352,48 @@ ORACLE_API int oracle_experts(int64_t n_tok, const int64_t* tokens, int32_t d, i
   free(sh);
   return status;
 }
+
+/* ---- O9: dense SwiGLU MLP block ---------------------------------------------
+ * The blocks before the first MoE block use a dense MLP instead of the MoE
+ * ([BLK]: the first first_k_dense_replace blocks; [MLP]: GlmMoeDsaMLP, three
+ * bias-free nn.Linear maps [out, in], down(silu(gate x) * up x)).  For every
+ * token t of the batch, with h the RMSNorm output (O1):
+ *   g_n = sum_i gate[n][i] h_i,  u_n = sum_i up[n][i] h_i,  a_n = silu(g_n) * u_n
+ *   y_m = sum_n down[m][n] a_n
+ *   out_m = D(x_m + y_m)            ([BLK]: the residual is the pre-norm input)
+ * fp64 accumulation, no intermediate rounding; optional act [T*Id] and y [T*d]. */
+ORACLE_API int oracle_dense_mlp(int64_t T, int32_t d, int32_t Id, int32_t dtype, const void* x,
+                                const float* h, const void* gate, const void* up,
+                                const void* down, double* delta, float* out, double* act_dbg) {
+  if (T < 0 || d <= 0 || Id <= 0) return -1;
+  if (T == 0) return 0;
+  if (!x || !h || !gate || !up || !down || !delta || !out) return -1;
+  int status = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = 0; t < T; ++t) {
+    const float* ht = h + t * d;
+    double* a = (double*)malloc(sizeof(double) * (size_t)Id);
+    if (!a) {
+#pragma omp atomic write
+      status = -1;
+      continue;
+    }
+    for (int32_t n = 0; n < Id; ++n) {
+      double g = 0.0, u = 0.0;
+      for (int32_t i = 0; i < d; ++i) {
+        g += (double)load_elem(gate, (int64_t)n * d + i, dtype) * (double)ht[i];
+        u += (double)load_elem(up, (int64_t)n * d + i, dtype) * (double)ht[i];
+      }
+      a[n] = silu(g) * u;
+      if (act_dbg) act_dbg[t * Id + n] = a[n];
+    }
+    for (int32_t m = 0; m < d; ++m) {
+      double y = 0.0;
+      for (int32_t n = 0; n < Id; ++n) y += (double)load_elem(down, (int64_t)m * Id + n, dtype) * a[n];
+      delta[t * d + m] = y;
+      out[t * d + m] = round_to_dtype((float)((double)load_elem(x, t * d + m, dtype) + y), dtype);
+    }
+    free(a);
+  }
+  return status;
+}

@@ -285,3 +285,65 @@ def test_rejects_bad_arguments():
         oracle.select(np.zeros((2, 4), np.float32), np.zeros(4, np.float32), 0, 1.0)
     with pytest.raises(TypeError):
         oracle.rmsnorm(np.zeros((2, 4), np.float32), np.zeros(4, np.float32), oracle.BF16)
+
+
+# ----------------------------------------------------------------------------- dense block
+def _dense_inputs(T, d, Id, dtype, seed):
+    x, norm_w = workloads.draw_norm(T, d, d, dtype, seed=seed)
+    w = workloads.draw_dense(d, Id, dtype, seed=seed)
+    return x, norm_w, w
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dense_block_matches_torch_library(dtype):
+    """The page's GlmMoeDsaMLP.forward is down_proj(act_fn(gate_proj(x)) * up_proj(x)) with
+    bias-free nn.Linear maps: evaluated here by torch.nn.functional in fp64 on the oracle's
+    (separately pinned) RMSNorm output, the dense-MLP oracle must agree to rounding."""
+    T, d, Id = 13, 256, 192
+    x, norm_w, w = _dense_inputs(T, d, Id, dtype, seed=5)
+    dt = oracle.DTYPES[dtype]
+    r = oracle.dense_block(x, norm_w, w["gate"], w["up"], w["down"], dt, debug=True)
+
+    def val(a):
+        return torch.from_numpy(bf16_bits_to_f32(a) if dtype == "bf16" else a).double()
+
+    h = torch.from_numpy(r["h"]).double()
+    act = F.silu(F.linear(h, val(w["gate"]))) * F.linear(h, val(w["up"]))
+    ref = F.linear(act, val(w["down"]))
+    np.testing.assert_allclose(r["act"], act.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(r["delta"], ref.numpy(), rtol=1e-10, atol=1e-12)
+    # out = x + delta rounded once (to fp32, then to D)
+    exact = (val(x) + ref).numpy()
+    tol = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -22
+    np.testing.assert_allclose(r["out"], exact, rtol=tol, atol=tol * 1e-3)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dense_block_equals_single_expert_moe_block(dtype):
+    """A dense block is the MoE block with one routed expert taken with weight 1 and no
+    shared expert: E = 1, k = 1, routed_scale = 1, gate_and_up[0] = [gate^T | up^T],
+    down[0] = down^T (the adapter's grouped orientation).  The two oracle paths must give
+    the same delta and out."""
+    T, d, Id = 9, 128, 64
+    x, norm_w, w = _dense_inputs(T, d, Id, dtype, seed=8)
+    dt = oracle.DTYPES[dtype]
+    r = oracle.dense_block(x, norm_w, w["gate"], w["up"], w["down"], dt)
+    gate_up = np.ascontiguousarray(np.concatenate([w["gate"].T, w["up"].T], axis=1))[None]
+    down = np.ascontiguousarray(w["down"].T)[None]
+    router_w = np.zeros((1, d), x.dtype)
+    inp = dict(x=x, norm_w=norm_w, router_w=router_w, corr_bias=np.zeros(1, np.float32),
+               gate_up=[gate_up[0]], down=[down[0]], shared_gate=None, shared_up=None,
+               shared_down=None, dtype=dtype, top_k=1, routed_scale=1.0, eps=1e-6)
+    m = oracle.forward(inp)
+    np.testing.assert_allclose(m["delta"], r["delta"], rtol=1e-13, atol=1e-15)
+    assert np.array_equal(m["out"], r["out"])
+
+
+def test_dense_block_zero_down_is_identity_and_linear_in_down():
+    T, d, Id = 7, 64, 64
+    x, norm_w, w = _dense_inputs(T, d, Id, "f32", seed=2)
+    r0 = oracle.dense_block(x, norm_w, w["gate"], w["up"], np.zeros_like(w["down"]), 0)
+    assert np.array_equal(r0["out"], x) and np.all(r0["delta"] == 0)
+    r1 = oracle.dense_block(x, norm_w, w["gate"], w["up"], w["down"], 0)
+    r3 = oracle.dense_block(x, norm_w, w["gate"], w["up"], 4 * w["down"], 0)  # exact scaling
+    np.testing.assert_allclose(r3["delta"], 4 * r1["delta"], rtol=1e-12, atol=1e-14)

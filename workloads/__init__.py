@@ -13,7 +13,7 @@ Random streams: NumPy ``Generator(PCG64)`` seeded by ``SeedSequence(seed,
 spawn_key=(tensor_id, ...))``.  Tensor ids: x 0, norm_w 1, router_w 2,
 corr_bias 3, gate_up 4, down 5, shared_gate 6, shared_up 7, shared_down 8,
 zipf rank permutation 9, row redraws 10; standalone RMSNorm inputs 11 (x), 12
-(per-feature scales), 13 (gain).  Values are drawn in fp32 and rounded
+(per-feature scales), 13 (gain); dense MLP weights 14 (gate), 15 (up), 16 (down).  Values are drawn in fp32 and rounded
 to bfloat16 (round to nearest even) for bf16 workloads.
 
 Expert weights of the GLM-5-sized workloads (19.4 GB in bf16) can instead be
@@ -33,6 +33,7 @@ import numpy as np
 TID_X, TID_NORM, TID_ROUTER, TID_BIAS, TID_GATE_UP, TID_DOWN = 0, 1, 2, 3, 4, 5
 TID_SH_GATE, TID_SH_UP, TID_SH_DOWN, TID_ZIPF, TID_REDRAW = 6, 7, 8, 9, 10
 TID_NORM_X, TID_NORM_SCALE, TID_NORM_GAIN = 11, 12, 13
+TID_DENSE_GATE, TID_DENSE_UP, TID_DENSE_DOWN = 14, 15, 16
 
 # Strength of the Zipf-shaped correction bias of the skewed workload.  Written by
 # tests/golden/calibrate_zipf.py (output tests/golden/zipf_beta.json): the value
@@ -313,3 +314,33 @@ def draw_norm(rows: int, width: int, stride: int, dtype: str, seed: int = 0):
     x = _rng(seed, TID_NORM_X).standard_normal((rows, stride), dtype=np.float32) * scale
     gain = (1.0 + 0.1 * _rng(seed, TID_NORM_GAIN).standard_normal(width)).astype(np.float32)
     return _store(x, dtype), _store(gain, dtype)
+
+
+# ----------------------------------------------------------------------------- dense MLP blocks
+@dataclasses.dataclass(frozen=True)
+class DenseCase:
+    """A dense block (RMSNorm + SwiGLU MLP + residual): T tokens, hidden d, MLP width Id."""
+    name: str
+    T: int
+    d: int
+    Id: int
+    dtype: str = "bf16"
+    eps: float = 1e-6
+
+
+# The blocks before the first MoE block use a dense SwiGLU MLP ("GLM-5 · Input
+# features", excerpt block: the first first_k_dense_replace blocks).  Its width
+# (intermediate_size) is not printed: 12288 (twice the hidden size) is synthetic.
+DENSE_CASES = {
+    "glm5_dense_decode": DenseCase("glm5_dense_decode", 64, 6144, 12288),
+    "glm5_dense_prefill": DenseCase("glm5_dense_prefill", 4096, 6144, 12288),
+}
+
+
+def draw_dense(d: int, Id: int, dtype: str, seed: int = 0) -> dict:
+    """Dense MLP weights in nn.Linear [out, in] layout: gate [Id, d], up [Id, d],
+    down [d, Id], each N(0, 0.02^2), storage dtype."""
+    gate = 0.02 * _rng(seed, TID_DENSE_GATE).standard_normal((Id, d), dtype=np.float32)
+    up = 0.02 * _rng(seed, TID_DENSE_UP).standard_normal((Id, d), dtype=np.float32)
+    down = 0.02 * _rng(seed, TID_DENSE_DOWN).standard_normal((d, Id), dtype=np.float32)
+    return dict(gate=_store(gate, dtype), up=_store(up, dtype), down=_store(down, dtype))
