@@ -216,6 +216,46 @@ def measure_norms(launches):
     return out
 
 
+def measure_dense(launches):
+    """Dense block (RMSNorm + SwiGLU MLP + residual; moe_dense_block_forward) at the
+    GLM-5 hidden size with a synthetic MLP width: tokens/s and the step against
+    max(bytes_alg / 8 TB/s, flops_alg / 2.5 PFLOP/s), bytes_alg = the three weight
+    matrices + x read + out written, flops_alg = 6 T d Id."""
+    import torch
+    import workloads
+    import mixture_experts_transformer_rmsnorm_amd as moe
+    out = {}
+    for name, c in workloads.DENSE_CASES.items():
+        tin, _ = workloads.make_dense_torch(c, 0, "cuda", weights="device")
+        blk = moe.DenseBlock({k: tin[k] for k in ("norm_w", "gate", "up", "down")}, max_tokens=c.T,
+                             eps=c.eps)
+        y = torch.empty_like(tin["x"])
+        for _ in range(3):
+            blk.forward(tin["x"], out=y)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(launches):
+            blk.forward(tin["x"], out=y)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        b = 2 if c.dtype == "bf16" else 4
+        nbytes = 3 * c.d * c.Id * b + 2 * c.T * c.d * b
+        flops = 6 * c.T * c.d * c.Id
+        t_hbm, t_mfma = nbytes / 8e12, flops / 2.5e15
+        out[name] = {"tokens": c.T, "dim": c.d, "mlp_width": c.Id, "ms": round(ms, 4),
+                     "tokens_per_s": round(c.T / (ms * 1e-3), 1),
+                     "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+                     "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "TFLOP_per_s": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "frac_of_max_roofline": round(max(t_hbm, t_mfma) / (ms * 1e-3), 4)}
+        log("dense %s: %.4f ms, %.1f tokens/s, %.1f%% of the max roofline" % (
+            name, ms, c.T / (ms * 1e-3), 100 * out[name]["frac_of_max_roofline"]))
+        blk.close()
+        del tin, blk, y
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,9 +266,9 @@ def main():
                     help="second workload of the same shape family reported in the line ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--extras", default="norms",
+    ap.add_argument("--extras", default="norms,dense",
                     help="comma list of extra entry points measured into the line's 'extras' "
-                         "('norms'; '' = none)")
+                         "('norms', 'dense'; '' = none)")
     ap.add_argument("--only-extras", action="store_true",
                     help="measure only the extras and print them as one JSON line (profiling)")
     ap.add_argument("--calib-mib", type=int, default=0,
@@ -259,6 +299,8 @@ def main():
         ext = {}
         if "norms" in extras_req:
             ext["rmsnorm"] = measure_norms(max(args.steps // 2, 5))
+        if "dense" in extras_req:
+            ext["dense_block"] = measure_dense(max(args.steps // 2, 5))
         return ext
 
     if args.only_extras:

@@ -95,10 +95,11 @@ typedef struct {
   uint32_t struct_size;  /* sizeof(moe_config_t) */
   int32_t dim;           /* d: multiple of 64 */
   int64_t max_tokens;    /* largest num_tokens a forward call may pass (>= 0) */
-  int32_t n_experts;     /* E: 1..1024 */
-  int32_t moe_inter;     /* I: multiple of 64 */
-  int32_t shared_inter;  /* Is: 0 (no shared expert) or a multiple of 64 */
-  int32_t max_top_k;     /* 1..min(E, 16) */
+  int32_t n_experts;     /* E: 1..1024; 0 makes a dense-block plan (see below) */
+  int32_t moe_inter;     /* I: multiple of 64 (0 for a dense-block plan) */
+  int32_t shared_inter;  /* Is: 0 (no shared expert) or a multiple of 64; for a
+                            dense-block plan, the MLP width (> 0) */
+  int32_t max_top_k;     /* 1..min(E, 16) (0 for a dense-block plan) */
   int32_t dtype;         /* moe_dtype_t */
   int32_t path;          /* moe_path_t */
   float eps;             /* RMSNorm epsilon (> 0) */
@@ -127,6 +128,30 @@ MOE_API moe_status_t moe_block_forward(moe_plan_t plan, void* workspace, size_t 
                                const void* down, const void* shared_gate, const void* shared_up,
                                const void* shared_down, int32_t top_k, float routed_scale,
                                void* out);
+
+/* Dense block: the blocks in front of the first MoE block use a dense SwiGLU MLP
+ * instead of the MoE ("GLM-5 · Input features", excerpt block: the first
+ * first_k_dense_replace blocks; excerpt mlp: GlmMoeDsaMLP, down(silu(gate x) *
+ * up x) with bias-free nn.Linear maps).  Per token t:
+ *
+ *   h   = RMSNorm(x) * norm_w          (as in moe_block_forward)
+ *   out = x + down(silu(h . gate^T) * (h . up^T))
+ *
+ * The plan comes from moe_plan_create with n_experts = 0, moe_inter = 0,
+ * max_top_k = 0 and shared_inter = Id, the MLP width (a multiple of 64).
+ * Layouts (row-major, contiguous, device memory, 16-byte aligned, dtype D):
+ *   x, out [T, d]; norm_w [d]; gate, up [Id, d]; down [d, Id]  (nn.Linear [out, in]).
+ * num_tokens in [0, max_tokens]; 0 is a successful no-op that reads no pointer.
+ * out may alias x.  Errors, ownership, workspace and stage timing as for
+ * moe_block_forward (stages rmsnorm, shared_gate_up, shared_act, shared_down,
+ * combine).  A dense plan passed to moe_block_forward, or a MoE plan passed
+ * here, returns NOT_SUPPORTED.  For a dense plan, moe_read_buffer and
+ * moe_buffer_bytes take top_k = 0 and serve MOE_BUF_H and MOE_BUF_SHARED_ACT (the
+ * MLP activation); moe_read_routing returns NOT_SUPPORTED. */
+MOE_API moe_status_t moe_dense_block_forward(moe_plan_t plan, void* workspace, size_t workspace_bytes,
+                                             void* stream, int64_t num_tokens, const void* x,
+                                             const void* norm_w, const void* gate, const void* up,
+                                             const void* down, void* out);
 
 /* Copy the routing of the last forward call that used `workspace` into caller
  * buffers (device memory), enqueued on `stream`:
@@ -186,7 +211,8 @@ MOE_API moe_status_t moe_read_buffer(moe_plan_t plan, const void* workspace, voi
 /* Size in bytes of intermediate buffer `which` for num_tokens/top_k (0 if invalid). */
 MOE_API size_t moe_buffer_bytes(moe_plan_t plan, int64_t num_tokens, int32_t top_k, int32_t which);
 
-/* Path the plan takes for num_tokens/top_k (MOE_PATH_STREAM or MOE_PATH_MFMA). */
+/* Path the plan takes for num_tokens/top_k (MOE_PATH_STREAM or MOE_PATH_MFMA); for
+ * a dense-block plan, MFMA for bf16 and STREAM (the fp32 FMA products) for fp32. */
 MOE_API int32_t moe_plan_path(moe_plan_t plan, int64_t num_tokens, int32_t top_k);
 
 /* Per-stage GPU timing.  stage_mask selects stages (bit s = stage s, see

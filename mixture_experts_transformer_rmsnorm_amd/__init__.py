@@ -36,7 +36,7 @@ ABI_VERSION = 1
 EXPORTS = ("moe_plan_create", "moe_plan_destroy", "moe_block_forward", "moe_read_routing",
            "moe_read_buffer", "moe_buffer_bytes", "moe_plan_path", "moe_set_stage_timing",
            "moe_stage_times", "moe_stage_name", "moe_status_string", "moe_abi_version",
-           "moe_rmsnorm")
+           "moe_rmsnorm", "moe_dense_block_forward")
 
 
 class MoEError(RuntimeError):
@@ -90,10 +90,12 @@ def load(path: str = LIB_PATH):
         lib.moe_status_string.argtypes = [i32]
         lib.moe_status_string.restype = ctypes.c_char_p
         lib.moe_rmsnorm.argtypes = [P, i32, i64, i32, ctypes.c_float, P, i64, P, P, i64]
+        lib.moe_dense_block_forward.argtypes = [P, P, ctypes.c_size_t, P, i64, P, P, P, P, P, P]
         lib.moe_abi_version.argtypes = []
         lib.moe_abi_version.restype = i32
         for fn in ("moe_plan_create", "moe_plan_destroy", "moe_block_forward", "moe_read_routing",
-                   "moe_read_buffer", "moe_set_stage_timing", "moe_stage_times", "moe_rmsnorm"):
+                   "moe_read_buffer", "moe_set_stage_timing", "moe_stage_times", "moe_rmsnorm",
+                   "moe_dense_block_forward"):
             getattr(lib, fn).restype = i32
         if lib.moe_abi_version() != ABI_VERSION:
             raise ImportError("libmoe_mi355x.so ABI %d != binding ABI %d"
@@ -193,6 +195,13 @@ def rmsnorm(x, weight, eps=1e-6, out=None, stream=None):
     moe_rmsnorm(stream, dt, x2.shape[0], width, eps, x2, x2.stride(0) if x2.shape[0] > 1 else width,
                 weight, o2, o2.stride(0) if o2.shape[0] > 1 else width)
     return out
+
+
+def moe_dense_block_forward(plan, workspace, workspace_bytes, stream, num_tokens, x, norm_w, gate,
+                            up, down, out) -> None:
+    _check(load().moe_dense_block_forward(plan, _ptr(workspace), workspace_bytes, _stream(stream),
+                                          num_tokens, _ptr(x), _ptr(norm_w), _ptr(gate), _ptr(up),
+                                          _ptr(down), _ptr(out)), "moe_dense_block_forward")
 
 
 def moe_read_routing(plan, workspace, stream, num_tokens, top_k, topk_idx=None, topk_w=None,
@@ -313,4 +322,57 @@ class MoEBlock:
         n = moe_buffer_bytes(self.plan, num_tokens, self.top_k, which)
         dst = torch.empty(max(n, 1), dtype=torch.uint8, device=self.workspace.device)
         moe_read_buffer(self.plan, self.workspace, stream, num_tokens, self.top_k, which, dst, n)
+        return dst[:n]
+
+
+class DenseBlock:
+    """A dense block (RMSNorm + SwiGLU MLP + residual): a dense-block plan, its device
+    workspace and the weights (torch tensors): norm_w [d], gate [Id, d], up [Id, d],
+    down [d, Id], as in ``include/moe.h``."""
+
+    def __init__(self, weights: dict, max_tokens: int, eps: float = 1e-6, device=None):
+        import torch
+        g = weights["gate"]
+        Id, d = g.shape
+        self.dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}[g.dtype]
+        self.weights = weights
+        self.dim, self.width = d, Id
+        self.cfg = make_config(d, max_tokens, 0, 0, Id, 0, self.dtype, MOE_PATH_AUTO, eps)
+        self.plan, self.workspace_bytes = moe_plan_create(self.cfg)
+        self.workspace = torch.empty(max(self.workspace_bytes, 1), dtype=torch.uint8,
+                                     device=device or g.device)
+
+    def close(self):
+        if self.plan:
+            moe_plan_destroy(self.plan)
+            self.plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def forward(self, x, out=None, stream=None):
+        """x: [..., d] tensor; returns out of the same shape (may be x itself)."""
+        import torch
+        shape = x.shape
+        x2 = x.reshape(-1, self.dim)
+        if not x2.is_contiguous():
+            raise ValueError("x must be contiguous")
+        if out is None:
+            out = torch.empty_like(x2)
+        w = self.weights
+        moe_dense_block_forward(self.plan, self.workspace, self.workspace_bytes, stream, x2.shape[0],
+                                x2, w["norm_w"], w["gate"], w["up"], w["down"], out)
+        return out.reshape(shape)
+
+    __call__ = forward
+
+    def buffer(self, which, num_tokens, stream=None):
+        """MOE_BUF_H or MOE_BUF_SHARED_ACT of the last call as a flat uint8 tensor."""
+        import torch
+        n = moe_buffer_bytes(self.plan, num_tokens, 0, which)
+        dst = torch.empty(max(n, 1), dtype=torch.uint8, device=self.workspace.device)
+        moe_read_buffer(self.plan, self.workspace, stream, num_tokens, 0, which, dst, n)
         return dst[:n]

@@ -204,9 +204,13 @@ moe_status_t moe_plan_create(const moe_config_t* cfg, moe_plan_t* plan, size_t* 
   if (!cfg || !plan || !workspace_bytes) return MOE_ERROR_INVALID_VALUE;
   *plan = nullptr;
   if (cfg->struct_size != sizeof(moe_config_t)) return MOE_ERROR_INVALID_VALUE;
-  if (cfg->dim <= 0 || cfg->n_experts <= 0 || cfg->moe_inter <= 0 || cfg->shared_inter < 0 ||
-      cfg->max_tokens < 0 || cfg->max_top_k < 1 || cfg->max_top_k > cfg->n_experts ||
+  // n_experts == 0: a dense block (its MLP is the shared_inter-wide SwiGLU; no router)
+  const bool dense = cfg->n_experts == 0;
+  if (cfg->dim <= 0 || cfg->n_experts < 0 || cfg->shared_inter < 0 || cfg->max_tokens < 0 ||
       !(cfg->eps > 0.0f) || !isfinite(cfg->eps) || cfg->flags != 0)
+    return MOE_ERROR_INVALID_VALUE;
+  if (dense ? (cfg->moe_inter != 0 || cfg->max_top_k != 0 || cfg->shared_inter == 0)
+            : (cfg->moe_inter <= 0 || cfg->max_top_k < 1 || cfg->max_top_k > cfg->n_experts))
     return MOE_ERROR_INVALID_VALUE;
   if (cfg->dtype != MOE_DTYPE_F32 && cfg->dtype != MOE_DTYPE_BF16) return MOE_ERROR_NOT_SUPPORTED;
   if (cfg->path < MOE_PATH_AUTO || cfg->path > MOE_PATH_MFMA) return MOE_ERROR_INVALID_VALUE;
@@ -240,6 +244,8 @@ moe_status_t moe_plan_destroy(moe_plan_t p) {
 
 int32_t moe_plan_path(moe_plan_t p, int64_t num_tokens, int32_t top_k) {
   if (!p) return -1;
+  if (p->cfg.n_experts == 0)  // dense plan: the family of its K-contiguous products
+    return p->cfg.dtype == MOE_DTYPE_BF16 ? MOE_PATH_MFMA : MOE_PATH_STREAM;
   return use_mfma(p, num_tokens, top_k) ? MOE_PATH_MFMA : MOE_PATH_STREAM;
 }
 
@@ -277,6 +283,7 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
                                void* out) {
   if (!p) return MOE_ERROR_INVALID_VALUE;
   const moe_config_t& c = p->cfg;
+  if (c.n_experts == 0) return MOE_ERROR_NOT_SUPPORTED;  // dense plan: moe_dense_block_forward
   if (T < 0 || T > c.max_tokens) return MOE_ERROR_INVALID_VALUE;
   if (k < 1 || k > c.max_top_k || k > c.n_experts) return MOE_ERROR_INVALID_VALUE;
   if (!isfinite(routed_scale)) return MOE_ERROR_INVALID_VALUE;
@@ -407,9 +414,88 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   return err == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
 }
 
-size_t moe_buffer_bytes(moe_plan_t p, int64_t T, int32_t k, int32_t which) {
-  if (!p || T < 0 || T > p->cfg.max_tokens || k < 1 || k > p->cfg.max_top_k) return 0;
+moe_status_t moe_dense_block_forward(moe_plan_t p, void* workspace, size_t workspace_bytes,
+                                     void* stream, int64_t T, const void* x, const void* norm_w,
+                                     const void* gate, const void* up, const void* down,
+                                     void* out) {
+  if (!p) return MOE_ERROR_INVALID_VALUE;
   const moe_config_t& c = p->cfg;
+  if (c.n_experts != 0) return MOE_ERROR_NOT_SUPPORTED;  // MoE plan: moe_block_forward
+  if (T < 0 || T > c.max_tokens) return MOE_ERROR_INVALID_VALUE;
+  if (T == 0) return MOE_SUCCESS;  // nothing is read or written
+  if (!workspace || !x || !norm_w || !gate || !up || !down || !out) return MOE_ERROR_INVALID_VALUE;
+  if (misaligned(workspace) || misaligned(x) || misaligned(norm_w) || misaligned(gate) ||
+      misaligned(up) || misaligned(down) || misaligned(out))
+    return MOE_ERROR_MISALIGNED;
+  if (workspace_bytes < p->lay.total) return MOE_ERROR_WORKSPACE_TOO_SMALL;
+
+  hipStream_t s = (hipStream_t)stream;
+  const Layout& L = p->lay;
+  char* ws = (char*)workspace;
+  void* h = ws + L.h;
+  float* sh_gu = (float*)(ws + L.sh_gu);
+  void* act_s = ws + L.act_s;
+  float* sh_dn = (float*)(ws + L.sh_dn);
+  const int dt = c.dtype == MOE_DTYPE_BF16 ? kBF16 : kF32;
+  const int d = c.dim, Id = c.shared_inter;
+  int tm, tn, tk;
+  nt_tiles(p, &tm, &tn, &tk);
+  const Split gsplit = nt_split(T, 2 * (int64_t)Id, d, tm, tn, tk, kMaxSharedSplits);
+  const Split dsplit = nt_split(T, d, Id, tm, tn, tk, kMaxSharedSplits);
+  auto nt = [&](const void* Aop, int64_t lda, const void* B1, const void* B2, int64_t ldb,
+                int n_split, float* outp, int64_t N, int64_t K, const Split& sp) {
+    NtArgs a{Aop, lda, B1, B2, ldb, n_split, outp, (int)T, (int)N, (int)K, sp.splits, sp.kt_per};
+    return dt == kBF16 ? launch_mfma_nt(a, s) : launch_fma_nt(dt, a, s);
+  };
+
+  int32_t tmask = 0;
+  std::unique_lock<std::mutex> tlock(p->tmu);
+  tmask = p->timing_mask;
+  if (tmask) ++p->timed_calls;
+  else tlock.unlock();
+  hipError_t err = hipSuccess;
+  auto stage = [&](int st, auto&& fn) {
+    if (err != hipSuccess) return;
+    EventPair ev{st, nullptr, nullptr};
+    const bool timing = (tmask >> st) & 1;
+    if (timing) {
+      ev.a = get_event(p);
+      ev.b = get_event(p);
+      if (!ev.a || !ev.b) {
+        err = hipErrorOutOfMemory;
+        return;
+      }
+      err = hipEventRecord(ev.a, s);
+      if (err != hipSuccess) return;
+    }
+    err = fn();
+    if (timing) {
+      const hipError_t e2 = hipEventRecord(ev.b, s);
+      if (err == hipSuccess) err = e2;
+      p->pending.push_back(ev);
+    }
+  };
+  // h = RMSNorm(x); act = silu(h gate^T) * (h up^T); out = x + act down^T
+  stage(kStNorm, [&] { return launch_rmsnorm(dt, x, d, norm_w, h, d, T, d, c.eps, s); });
+  stage(kStSharedGateUp, [&] { return nt(h, d, gate, up, d, Id, sh_gu, 2 * (int64_t)Id, d, gsplit); });
+  stage(kStSharedAct, [&] { return launch_swiglu_finalize(dt, sh_gu, gsplit.splits, T, Id, act_s, s); });
+  stage(kStSharedDown, [&] { return nt(act_s, Id, down, down, Id, d, sh_dn, d, Id, dsplit); });
+  stage(kStCombine, [&] {
+    return launch_combine(dt, x, sh_dn, dsplit.splits, nullptr, nullptr, nullptr, T, d, 0, out, s);
+  });
+  return err == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
+}
+
+size_t moe_buffer_bytes(moe_plan_t p, int64_t T, int32_t k, int32_t which) {
+  if (!p || T < 0 || T > p->cfg.max_tokens) return 0;
+  const moe_config_t& c = p->cfg;
+  if (c.n_experts == 0) {  // dense plan: h and the MLP activation, k must be 0
+    if (k != 0) return 0;
+    if (which == MOE_BUF_H) return (size_t)T * c.dim * p->es;
+    if (which == MOE_BUF_SHARED_ACT) return (size_t)T * c.shared_inter * p->es;
+    return 0;
+  }
+  if (k < 1 || k > c.max_top_k) return 0;
   const int64_t A = T * k;
   switch (which) {
     case MOE_BUF_H: return (size_t)T * c.dim * p->es;
@@ -450,7 +536,12 @@ moe_status_t moe_read_buffer(moe_plan_t p, const void* workspace, void* stream, 
                              int32_t k, int32_t which, void* dst, size_t dst_bytes) {
   if (!p || !workspace || !dst) return MOE_ERROR_INVALID_VALUE;
   if (which < 0 || which >= MOE_BUF_COUNT) return MOE_ERROR_INVALID_VALUE;
-  if (T < 0 || T > p->cfg.max_tokens || k < 1 || k > p->cfg.max_top_k) return MOE_ERROR_INVALID_VALUE;
+  if (T < 0 || T > p->cfg.max_tokens) return MOE_ERROR_INVALID_VALUE;
+  if (p->cfg.n_experts == 0) {  // dense plan: k = 0; only h and the MLP activation exist
+    if (k != 0 || (which != MOE_BUF_H && which != MOE_BUF_SHARED_ACT)) return MOE_ERROR_INVALID_VALUE;
+  } else if (k < 1 || k > p->cfg.max_top_k) {
+    return MOE_ERROR_INVALID_VALUE;
+  }
   const size_t bytes = moe_buffer_bytes(p, T, k, which);
   if (dst_bytes < bytes) return MOE_ERROR_INVALID_VALUE;
   if (bytes == 0) return MOE_SUCCESS;
@@ -472,6 +563,7 @@ moe_status_t moe_read_buffer(moe_plan_t p, const void* workspace, void* stream, 
 
 moe_status_t moe_read_routing(moe_plan_t p, const void* workspace, void* stream, int64_t T,
                               int32_t k, int32_t* topk_idx, float* topk_w, int32_t* counts) {
+  if (p && p->cfg.n_experts == 0) return MOE_ERROR_NOT_SUPPORTED;  // dense plan: no routing
   if (!p || !workspace) return MOE_ERROR_INVALID_VALUE;
   if (T < 0 || T > p->cfg.max_tokens || k < 1 || k > p->cfg.max_top_k) return MOE_ERROR_INVALID_VALUE;
   const Layout& L = p->lay;

@@ -172,3 +172,54 @@ def test_rmsnorm_validation(kw, status):
                                  args["x"], args["x_stride"], args["weight"], args["out"],
                                  args["out_stride"])
     assert got == status
+
+
+def _dense_cfg(**kw):
+    base = dict(dim=6144, max_tokens=64, n_experts=0, moe_inter=0, shared_inter=12288,
+                max_top_k=0, dtype="bf16")
+    base.update(kw)
+    return moe.make_config(**base)
+
+
+@pytest.mark.parametrize("kw", [dict(moe_inter=64), dict(max_top_k=1), dict(shared_inter=0),
+                                dict(n_experts=-1)])
+def test_dense_plan_validation(kw):
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_plan_create(_dense_cfg(**kw))
+    assert ei.value.status == moe.MOE_ERROR_INVALID_VALUE
+
+
+def test_dense_plan_entry_points_and_buffers():
+    plan, ws = moe.moe_plan_create(_dense_cfg(max_tokens=4096))
+    moe_plan, _ = moe.moe_plan_create(_cfg())
+    lib = moe.load()
+    try:
+        assert ws >= 4096 * 12288 * 2  # the MLP activation in bf16
+        assert moe.moe_plan_path(plan, 64, 0) == moe.MOE_PATH_MFMA
+        assert moe.moe_buffer_bytes(plan, 10, 0, moe.MOE_BUF_H) == 10 * 6144 * 2
+        assert moe.moe_buffer_bytes(plan, 10, 0, moe.MOE_BUF_SHARED_ACT) == 10 * 12288 * 2
+        assert moe.moe_buffer_bytes(plan, 10, 1, moe.MOE_BUF_H) == 0
+        assert moe.moe_buffer_bytes(plan, 10, 0, moe.MOE_BUF_Y) == 0
+        X = 0x100000
+        # wrong plan kind, either way round
+        assert lib.moe_block_forward(plan, X, ws, 0, 4, X, X, X, X, X, X, X, X, X, 1, 1.0, X) == \
+            moe.MOE_ERROR_NOT_SUPPORTED
+        assert lib.moe_dense_block_forward(moe_plan, X, ws, 0, 4, X, X, X, X, X, X) == \
+            moe.MOE_ERROR_NOT_SUPPORTED
+        assert lib.moe_read_routing(plan, X, 0, 4, 1, X, X, X) == moe.MOE_ERROR_NOT_SUPPORTED
+        # argument checks before any device work
+        assert lib.moe_dense_block_forward(plan, X, ws, 0, 4097, X, X, X, X, X, X) == \
+            moe.MOE_ERROR_INVALID_VALUE
+        assert lib.moe_dense_block_forward(plan, X, ws, 0, 4, X, X, None, X, X, X) == \
+            moe.MOE_ERROR_INVALID_VALUE
+        assert lib.moe_dense_block_forward(plan, X, ws, 0, 4, X, X, X, X + 8, X, X) == \
+            moe.MOE_ERROR_MISALIGNED
+        assert lib.moe_dense_block_forward(plan, X, ws - 1, 0, 4, X, X, X, X, X, X) == \
+            moe.MOE_ERROR_WORKSPACE_TOO_SMALL
+        assert lib.moe_dense_block_forward(plan, None, 0, 0, 0, None, None, None, None, None,
+                                           None) == moe.MOE_SUCCESS
+        assert lib.moe_read_buffer(plan, X, 0, 4, 0, moe.MOE_BUF_Y, X, 1 << 20) == \
+            moe.MOE_ERROR_INVALID_VALUE
+    finally:
+        moe.moe_plan_destroy(plan)
+        moe.moe_plan_destroy(moe_plan)

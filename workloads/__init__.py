@@ -344,3 +344,32 @@ def draw_dense(d: int, Id: int, dtype: str, seed: int = 0) -> dict:
     up = 0.02 * _rng(seed, TID_DENSE_UP).standard_normal((Id, d), dtype=np.float32)
     down = 0.02 * _rng(seed, TID_DENSE_DOWN).standard_normal((d, Id), dtype=np.float32)
     return dict(gate=_store(gate, dtype), up=_store(up, dtype), down=_store(down, dtype))
+
+
+def draw_block_input(T: int, d: int, dtype: str, seed: int = 0):
+    """x [T, d] ~ N(0, 1) and norm_w = 1 + 0.1 N(0, 1): the residual-stream input of a
+    block, drawn from the same streams (and so equal to) ``draw_small``'s x and norm_w."""
+    x = _rng(seed, TID_X).standard_normal((T, d), dtype=np.float32)
+    norm_w = (1.0 + 0.1 * _rng(seed, TID_NORM).standard_normal(d)).astype(np.float32)
+    return _store(x, dtype), _store(norm_w, dtype)
+
+
+def make_dense_torch(case, seed: int = 0, device="cuda", weights="device", T: Optional[int] = None):
+    """Inputs of a dense block as torch tensors plus the host x / norm_w: x and norm_w from
+    ``draw_block_input`` (the recipe of the MoE block's input); weights drawn on the
+    device with torch's generator (seeded per tensor) or, with weights="host", by
+    ``draw_dense``."""
+    torch = _torch()
+    T = case.T if T is None else T
+    dt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    x, norm_w = draw_block_input(T, case.d, case.dtype, seed)
+    out = dict(x=host_to_torch(x, case.dtype, device), norm_w=host_to_torch(norm_w, case.dtype, device))
+    if weights == "host":
+        w = draw_dense(case.d, case.Id, case.dtype, seed)
+        for key in ("gate", "up", "down"):
+            out[key] = host_to_torch(w[key], case.dtype, device)
+    else:
+        out["gate"] = _device_normal((case.Id, case.d), 0.02, _torch_seed(seed, TID_DENSE_GATE), dt, device)
+        out["up"] = _device_normal((case.Id, case.d), 0.02, _torch_seed(seed, TID_DENSE_UP), dt, device)
+        out["down"] = _device_normal((case.d, case.Id), 0.02, _torch_seed(seed, TID_DENSE_DOWN), dt, device)
+    return out, dict(x=x, norm_w=norm_w)
