@@ -185,6 +185,212 @@ __global__ __launch_bounds__(256) void mfma_nt_kernel(MfmaProblem p) {
 }
 
 // ---------------------------------------------------------------------------
+// Dense kernel for many rows (mfma_nt_big_kernel): the same product as
+// mfma_nt_kernel, 256 x 256 per block, 8 wavefronts in a 2 (M) x 4 (N)
+// arrangement, each owning the interleaved 32-row sub-tiles wm, wm+2, wm+4,
+// wm+6 and two 32-column groups (sub-tiles past the last row skip their MFMAs).
+// Both operands are K-contiguous and move global -> LDS directly
+// (global_load_lds_dwordx4) in K-steps of 64, whole 128-byte row pieces,
+// through rings of 32 KiB slots, 2 for A (rows of the left operand) and 3 for B
+// (rows of the right one, the weights): while step t is multiplied, A of step
+// t+1 and B of steps t+1 and t+2 are in flight.  Row r's
+// k-chunk c (8 elements) sits at chunk position c ^ ((r >> 1) & 7) of its
+// 128-byte LDS row (chosen on the load side), so the 16-byte fragment reads of
+// 16 consecutive rows hit distinct banks.  A and B fragments are both plain
+// 16-byte LDS reads.
+constexpr int NB_M = kNtBigTile, NB_N = kNtBigTile, NB_K = kMfmaBK, NB_THREADS = 512;
+constexpr int NB_TILE_ELEMS = NB_M * NB_K;  // 32 KiB per operand and slot
+static_assert(5 * NB_TILE_ELEMS * 2 <= 160 * 1024, "rings fit the LDS of a CU");
+static_assert(NB_TILE_ELEMS == NB_THREADS * 8 * 4, "4 loads per thread and operand");
+
+typedef __attribute__((address_space(3))) void lds_void_nt_t;
+
+__global__ __launch_bounds__(NB_THREADS) void mfma_nt_big_kernel(MfmaProblem p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sa0[NB_TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sa1[NB_TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sb0[NB_TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sb1[NB_TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sb2[NB_TILE_ELEMS];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Tiles are numbered in groups of 8 M-tiles: inside a group M-tile fastest, then
+  // N-tile; then the next group; then the split.  The numbers are dealt to the 8
+  // XCDs in contiguous ranges, so the 32 blocks an XCD runs at a time cover about
+  // 8 M-tiles x 4 N-tiles and share their A and B rows through its L2.
+  const int m_tiles = (p.M + NB_M - 1) / NB_M, n_tiles = (p.N + NB_N - 1) / NB_N;
+  const int nkt = p.K / NB_K;
+  const int splits = (nkt + p.kt_per_split - 1) / p.kt_per_split;
+  const int total = m_tiles * n_tiles * splits;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= per) return;
+  const int logical = (blockIdx.x % kXcds) * per + slot;
+  if (logical >= total) return;
+  constexpr int kGroupM = 8;
+  const int z = logical / (m_tiles * n_tiles);
+  const int l = logical % (m_tiles * n_tiles);
+  const int gm0 = (l / (kGroupM * n_tiles)) * kGroupM;  // first M-tile of l's group
+  const int gsz = min(kGroupM, m_tiles - gm0);          // M-tiles in that group
+  const int lg = l - gm0 * n_tiles;                     // index inside the group
+  const int m_tile = gm0 + lg % gsz;
+  const int n_tile = lg / gsz;
+  const int m0 = m_tile * NB_M, n0 = n_tile * NB_N;
+  const int rows = min(NB_M, p.M - m0);
+  const int kt0 = z * p.kt_per_split;
+  const int kt1 = min(nkt, kt0 + p.kt_per_split);
+
+  // Load side.  Instruction i (0..3) of wave w fills rows 8*(4w+i) .. +7 of a
+  // slot (lane/8 picks the row, lane%8 the chunk position).  A row groups that
+  // lie entirely past the last row are not loaded (rows past it inside a partly
+  // valid group repeat the last row); B rows past N read row 0.  Every load is
+  // in bounds, and what the clamped ones bring only reaches outputs that are
+  // never stored.
+  const uint16_t* a_src[4];
+  const uint16_t* b_src[4];
+  int a_groups = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * (4 * w + i) + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    a_src[i] = p.A + (int64_t)(m0 + min(r, rows - 1)) * p.lda + c * 8;
+    a_groups += 8 * (4 * w + i) < rows ? 1 : 0;
+    const int n = n0 + r < p.N ? n0 + r : 0;
+    const uint16_t* brow = n < p.n_split ? p.B1 + (int64_t)n * p.ldb
+                                         : p.B2 + (int64_t)(n - p.n_split) * p.ldb;
+    b_src[i] = brow + c * 8;
+  }
+  a_groups = __builtin_amdgcn_readfirstlane(a_groups);
+  auto issue_a = [&](uint16_t* da, int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < a_groups)
+        __builtin_amdgcn_global_load_lds(a_src[i] + kt * NB_K,
+                                         (lds_void_nt_t*)(da + (4 * w + i) * 512), 16, 0, 0);
+  };
+  auto issue_b = [&](uint16_t* db, int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(b_src[i] + kt * NB_K,
+                                       (lds_void_nt_t*)(db + (4 * w + i) * 512), 16, 0, 0);
+  };
+
+  // Compute side.
+  const int wm = w >> 2, wn = w & 3;
+  bool sub_ok[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sub_ok[j] = 32 * (wm + 2 * j) < rows;
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int f = 0; f < 2; ++f) acc[j][f] = f32x16_t{};
+  const int ar = wm * 32 + (lane & 31);       // A row of sub-tile 0 (sub-tile j: + 64 j)
+  const int br = wn * 64 + (lane & 31);       // B row of column group 0 (group f: + 32 f)
+  const int a_sw = (ar >> 1) & 7, b_sw0 = (br >> 1) & 7, b_sw1 = ((br + 32) >> 1) & 7;
+
+  // All four sub-tiles are multiplied whatever the row count (rows past the last
+  // one hold stale or repeated data and are never stored), so the MFMA stream has
+  // no branches; the fragments of k-substep ks+1 are read while the MFMAs of ks run.
+  auto compute = [&](const uint16_t* as, const uint16_t* bs) __attribute__((always_inline)) {
+    bf16x8_t af[2][4], bf[2][2];
+    auto load = [&](int ks, int buf) __attribute__((always_inline)) {
+      const int c = 2 * ks + (lane >> 5);
+      bf[buf][0] = *reinterpret_cast<const bf16x8_t*>(bs + br * NB_K + ((c ^ b_sw0) * 8));
+      bf[buf][1] = *reinterpret_cast<const bf16x8_t*>(bs + (br + 32) * NB_K + ((c ^ b_sw1) * 8));
+      const int a_chunk = (c ^ a_sw) * 8;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        af[buf][j] = *reinterpret_cast<const bf16x8_t*>(as + (ar + 64 * j) * NB_K + a_chunk);
+    };
+    load(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < NB_K / 16; ++ks) {
+      if (ks + 1 < NB_K / 16) load(ks + 1, (ks + 1) & 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][j], bf[ks & 1][0], acc[j][0], 0, 0, 0);
+        acc[j][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][j], bf[ks & 1][1], acc[j][1], 0, 0, 0);
+      }
+    }
+  };
+
+  // Step t: wait until only this wave's B loads of step t+2 are outstanding (A of
+  // step t+1, issued just before them, and B of step t+1, issued a step earlier,
+  // have landed; so has all of step t), barrier (every wave's data of step t has
+  // landed and every wave is done with the slots of step t-1), refill those slots
+  // with A of step t+1 and B of step t+2, multiply step t.  Steps past the end
+  // are copies of the last one, so that every step has the same count of loads in
+  // flight; they land in slots that are never read again.
+  auto step = [&](const uint16_t* a_cur, uint16_t* a_next, const uint16_t* b_cur, uint16_t* b_next,
+                  int t) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0070 | 4);  // vmcnt(4) lgkmcnt(0)
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(a_next, min(t + 1, kt1 - 1));
+    issue_b(b_next, min(t + 2, kt1 - 1));
+    compute(a_cur, b_cur);
+    // Order of the step's instructions: the 8 loads, the fragments of k-substep 0,
+    // then each substep's 8 MFMAs with the next substep's 6 fragment reads between
+    // them, so that LDS latency hides under the MFMAs.
+    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int ks = 0; ks < NB_K / 16 - 1; ++ks) {
+#pragma unroll
+      for (int q = 0; q < 6; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  };
+
+  if (kt0 < kt1) {
+    issue_b(sb0, kt0);
+    issue_a(sa0, kt0);
+    issue_b(sb1, min(kt0 + 1, kt1 - 1));
+    int t = kt0;
+    for (; t + 6 <= kt1; t += 6) {
+      step(sa0, sa1, sb0, sb2, t);
+      step(sa1, sa0, sb1, sb0, t + 1);
+      step(sa0, sa1, sb2, sb1, t + 2);
+      step(sa1, sa0, sb0, sb2, t + 3);
+      step(sa0, sa1, sb1, sb0, t + 4);
+      step(sa1, sa0, sb2, sb1, t + 5);
+    }
+    if (t < kt1) step(sa0, sa1, sb0, sb2, t);
+    if (t + 1 < kt1) step(sa1, sa0, sb1, sb0, t + 1);
+    if (t + 2 < kt1) step(sa0, sa1, sb2, sb1, t + 2);
+    if (t + 3 < kt1) step(sa1, sa0, sb0, sb2, t + 3);
+    if (t + 4 < kt1) step(sa0, sa1, sb1, sb0, t + 4);
+    // no load may still be writing LDS when the block ends
+    __builtin_amdgcn_s_waitcnt(0x0070);
+  }
+
+  const int col32 = lane & 31;
+  float* out = (float*)p.C + (int64_t)z * p.M * p.N;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (!sub_ok[j]) continue;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int n = n0 + wn * 64 + f * 32 + col32;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 32 * (wm + 2 * j) + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        if (r < rows) out[(int64_t)(m0 + r) * p.N + n] = acc[j][f][i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Grouped expert kernel (prefill-sized batches).
 //
 // Work unit: one M-tile (up to 256 permuted rows of one expert) x one N-tile
@@ -440,8 +646,16 @@ hipError_t launch_mfma_nt(const NtArgs& a, hipStream_t s) {
   p.M = a.M;
   p.kt_per_split = a.k_tiles_per_split;
   p.C = a.out;
-  dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, a.splits);
-  mfma_nt_kernel<<<grid, 256, 0, s>>>(p);
+  int tm, tn, tk;
+  mfma_nt_tile(a.M, &tm, &tn, &tk);
+  if (tm == NB_M) {
+    const int64_t tiles = (int64_t)((a.M + NB_M - 1) / NB_M) * ((a.N + NB_N - 1) / NB_N) * a.splits;
+    const int64_t blocks = (tiles + kXcds - 1) / kXcds * kXcds;
+    mfma_nt_big_kernel<<<dim3((unsigned)blocks), NB_THREADS, 0, s>>>(p);
+  } else {
+    dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, a.splits);
+    mfma_nt_kernel<<<grid, 256, 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 

@@ -22,6 +22,18 @@ constexpr int kMfmaBK = 64;
 // Tile of the fp32 FMA GEMM (router / shared expert of fp32 plans).
 constexpr int kFmaTile = 32;
 
+// Tile (rows, columns, K-step) of the bf16 dense K-contiguous product for M rows:
+// the direct-to-LDS kernel's 256 x 256 x 64 from 256 rows on, else the
+// register-staged kernel's 128 x 128 x 64.  Host split-K sizing and the launcher
+// both use this, so they agree on the tile.
+constexpr int kNtBigTile = 256;
+inline void mfma_nt_tile(int64_t M, int* tm, int* tn, int* tk) {
+  const bool big = M >= kNtBigTile;
+  *tm = big ? kNtBigTile : kMfmaBM;
+  *tn = big ? kNtBigTile : kMfmaBN;
+  *tk = kMfmaBK;
+}
+
 // Device-side routing summary written by the scan kernel.
 struct RouteHeader {
   int32_t n_active;  // experts with at least one token

@@ -103,26 +103,27 @@ bool use_mfma(const moe_plan* p, int64_t T, int k) {
   return T * k > (int64_t)kStreamMaxMeanTokens * p->cfg.n_experts;
 }
 
-// Tile sizes of the dense K-contiguous products for this plan's dtype.
-void nt_tiles(const moe_plan* p, int* tm, int* tn, int* tk) {
+// Tile sizes of the dense K-contiguous products of T rows for this plan's dtype.
+void nt_tiles(const moe_plan* p, int64_t T, int* tm, int* tn, int* tk) {
   if (p->cfg.dtype == MOE_DTYPE_BF16) {
-    *tm = kMfmaBM;
-    *tn = kMfmaBN;
-    *tk = kMfmaBK;
+    mfma_nt_tile(T, tm, tn, tk);
   } else {
     *tm = *tn = *tk = kFmaTile;
   }
 }
 
-// Largest split-K partial buffer (in fp32 elements) over every T <= Tmax.
+// Largest split-K partial buffer (in fp32 elements) over every T <= Tmax.  The split
+// count only changes where the tile count does, at multiples of the row tile (a
+// multiple of 32), so the multiples of 32 and Tmax itself cover every maximum.
 size_t max_partial_elems(const moe_plan* p, int64_t Tmax, int64_t N, int64_t K, int max_splits) {
-  int tm, tn, tk;
-  nt_tiles(p, &tm, &tn, &tk);
   size_t best = 0;
-  for (int64_t m = 1; m <= std::max<int64_t>(1, cdiv(Tmax, tm)); ++m) {
-    const int64_t T = std::min<int64_t>(m * tm, std::max<int64_t>(Tmax, 1));
+  const int64_t top = std::max<int64_t>(Tmax, 1);
+  for (int64_t T = std::min<int64_t>(32, top);; T = std::min<int64_t>(T + 32, top)) {
+    int tm, tn, tk;
+    nt_tiles(p, T, &tm, &tn, &tk);
     const Split s = nt_split(T, N, K, tm, tn, tk, max_splits);
     best = std::max(best, (size_t)s.splits * (size_t)T * (size_t)N);
+    if (T == top) break;
   }
   return best;
 }
@@ -325,7 +326,7 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   const int nchunks = (int)cdiv(T, kChunkTokens);
   const bool mfma = use_mfma(p, T, k);
   int tm, tn, tk;
-  nt_tiles(p, &tm, &tn, &tk);
+  nt_tiles(p, T, &tm, &tn, &tk);
 
   std::unique_lock<std::mutex> tlock(p->tmu, std::defer_lock);
   int32_t tmask = 0;
@@ -439,7 +440,7 @@ moe_status_t moe_dense_block_forward(moe_plan_t p, void* workspace, size_t works
   const int dt = c.dtype == MOE_DTYPE_BF16 ? kBF16 : kF32;
   const int d = c.dim, Id = c.shared_inter;
   int tm, tn, tk;
-  nt_tiles(p, &tm, &tn, &tk);
+  nt_tiles(p, T, &tm, &tn, &tk);
   const Split gsplit = nt_split(T, 2 * (int64_t)Id, d, tm, tn, tk, kMaxSharedSplits);
   const Split dsplit = nt_split(T, d, Id, tm, tn, tk, kMaxSharedSplits);
   auto nt = [&](const void* Aop, int64_t lda, const void* B1, const void* B2, int64_t ldb,

@@ -45,7 +45,7 @@ def _check(case, tin, host, g, tokens):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("T,d,Id", [(1, 256, 192), (37, 256, 320), (300, 512, 1024)])
+@pytest.mark.parametrize("T,d,Id", [(1, 256, 192), (37, 256, 320), (260, 256, 320), (300, 512, 1024)])
 def test_small_dense_blocks(T, d, Id, dtype):
     case = workloads.DenseCase("small", T, d, Id, dtype)
     say("dense %s T %d d %d Id %d" % (dtype, T, d, Id))
