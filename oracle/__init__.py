@@ -250,3 +250,28 @@ def dense_block(x, norm_w, gate, up, down, dtype, eps=1e-6, debug=False):
     if debug:
         res["act"] = r[2]
     return res
+
+
+def pack_expert(gate, up, down):
+    """Step O10: one expert's weights from the HF checkpoint layout (nn.Linear [out, in]:
+    gate_proj.weight [I, d], up_proj.weight [I, d], down_proj.weight [d, I]) to the grouped
+    native layout of Glm4MoeStateDictAdapter: its slice of gate_and_up_projs [d, 2I] (gate
+    columns first, then up) and of down_projs [I, d].  Storage arrays of any dtype; the
+    result holds the same elements, moved."""
+    gate, up, down = (np.asarray(a) for a in (gate, up, down))
+    I, d = gate.shape
+    if up.shape != (I, d) or down.shape != (d, I):
+        raise ValueError("pack_expert: gate %s up %s down %s" % (gate.shape, up.shape, down.shape))
+    gate_up = np.ascontiguousarray(np.concatenate([gate.T, up.T], axis=1))
+    return gate_up, np.ascontiguousarray(down.T)
+
+
+def unpack_expert(gate_up, down):
+    """Inverse of pack_expert: ([d, 2I], [I, d]) -> (gate [I, d], up [I, d], down [d, I])."""
+    gate_up, down = np.asarray(gate_up), np.asarray(down)
+    d, I2 = gate_up.shape
+    I = I2 // 2
+    if I2 != 2 * I or down.shape != (I, d):
+        raise ValueError("unpack_expert: gate_up %s down %s" % (gate_up.shape, down.shape))
+    return (np.ascontiguousarray(gate_up[:, :I].T), np.ascontiguousarray(gate_up[:, I:].T),
+            np.ascontiguousarray(down.T))

@@ -347,3 +347,46 @@ def test_dense_block_zero_down_is_identity_and_linear_in_down():
     r1 = oracle.dense_block(x, norm_w, w["gate"], w["up"], w["down"], 0)
     r3 = oracle.dense_block(x, norm_w, w["gate"], w["up"], 4 * w["down"], 0)  # exact scaling
     np.testing.assert_allclose(r3["delta"], 4 * r1["delta"], rtol=1e-12, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------- layout packing
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_packed_hf_weights_give_the_hf_mlp(dtype):
+    """HF per-expert weights packed into the grouped layout, run through the MoE oracle
+    (E = 1, k = 1, rs = 1, no shared expert), equal the page's SwiGLU MLP evaluated by
+    torch.nn.functional.linear directly on the HF [out, in] weights: this pins the packing
+    orientation (gate columns first, transposes) independently of the oracle's own code."""
+    T, d, I = 11, 128, 64
+    x, norm_w = workloads.draw_block_input(T, d, dtype, seed=4)
+    w = workloads.draw_dense(d, I, dtype, seed=4)      # stands in for one HF expert
+    gate_up, down = oracle.pack_expert(w["gate"], w["up"], w["down"])
+    assert gate_up.shape == (d, 2 * I) and down.shape == (I, d)
+    inp = dict(x=x, norm_w=norm_w, router_w=np.zeros((1, d), x.dtype),
+               corr_bias=np.zeros(1, np.float32), gate_up=[gate_up], down=[down],
+               shared_gate=None, shared_up=None, shared_down=None, dtype=dtype, top_k=1,
+               routed_scale=1.0, eps=1e-6)
+    r = oracle.forward(inp)
+
+    def val(a):
+        return torch.from_numpy(bf16_bits_to_f32(a) if dtype == "bf16" else a).double()
+
+    h = torch.from_numpy(r["h"]).double()
+    ref = F.linear(F.silu(F.linear(h, val(w["gate"]))) * F.linear(h, val(w["up"])), val(w["down"]))
+    np.testing.assert_allclose(r["delta"], ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_pack_unpack_round_trip_and_element_map():
+    d, I = 24, 8
+    gate = np.arange(I * d, dtype=np.float32).reshape(I, d)
+    up = 1000 + np.arange(I * d, dtype=np.float32).reshape(I, d)
+    down = 5000 + np.arange(d * I, dtype=np.float32).reshape(d, I)
+    gu, dn = oracle.pack_expert(gate, up, down)
+    # element map written out by hand: gu[i][n] = gate[n][i], gu[i][I+n] = up[n][i], dn[n][m] = down[m][n]
+    for i in (0, 5, d - 1):
+        for n in (0, 3, I - 1):
+            assert gu[i, n] == gate[n, i] and gu[i, I + n] == up[n, i]
+    for n in (0, I - 1):
+        for m in (0, 7, d - 1):
+            assert dn[n, m] == down[m, n]
+    g2, u2, d2 = oracle.unpack_expert(gu, dn)
+    assert np.array_equal(g2, gate) and np.array_equal(u2, up) and np.array_equal(d2, down)
