@@ -256,6 +256,52 @@ def measure_dense(launches):
     return out
 
 
+def measure_pack(launches, experts=32):
+    """Expert layout conversion (moe_pack_expert / moe_unpack_expert) at the GLM-5 expert
+    shape (d 6144, I 2048, bf16): HBM roofline with algorithmic bytes = each expert's
+    three matrices read once and written once, over `experts` experts per pass."""
+    import torch
+    import mixture_experts_transformer_rmsnorm_amd as moe
+    d, I = 6144, 2048
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    hf = [torch.randn((experts, I, d), generator=g, device="cuda").to(torch.bfloat16),
+          torch.randn((experts, I, d), generator=g, device="cuda").to(torch.bfloat16),
+          torch.randn((experts, d, I), generator=g, device="cuda").to(torch.bfloat16)]
+    gu = torch.empty((experts, d, 2 * I), dtype=torch.bfloat16, device="cuda")
+    dn = torch.empty((experts, I, d), dtype=torch.bfloat16, device="cuda")
+    back = [torch.empty_like(t) for t in hf]
+    out = {}
+    nbytes = 2 * 3 * experts * d * I * 2
+    for name in ("pack", "unpack"):
+        def one_pass():
+            for e in range(experts):
+                if name == "pack":
+                    moe.moe_pack_expert(None, moe.MOE_DTYPE_BF16, d, I, hf[0][e], hf[1][e], hf[2][e],
+                                        gu[e], dn[e])
+                else:
+                    moe.moe_unpack_expert(None, moe.MOE_DTYPE_BF16, d, I, gu[e], dn[e], back[0][e],
+                                          back[1][e], back[2][e])
+        one_pass()
+        passes = max(2, launches // 10)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(passes):
+            one_pass()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / passes
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"experts": experts, "dim": d, "moe_inter": I, "ms_per_pass": round(ms, 4),
+                     "algorithmic_bytes": nbytes, "GB_per_s": round(gbs, 1),
+                     "frac_of_hbm_peak": round(gbs / 8000.0, 4)}
+        log("%s %d experts: %.3f ms, %.1f GB/s" % (name, experts, ms, gbs))
+    ok = all(torch.equal(a, b) for a, b in zip(hf, back))
+    out["round_trip_identical"] = bool(ok)
+    del hf, gu, dn, back
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,9 +312,9 @@ def main():
                     help="second workload of the same shape family reported in the line ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--extras", default="norms,dense",
+    ap.add_argument("--extras", default="norms,dense,pack",
                     help="comma list of extra entry points measured into the line's 'extras' "
-                         "('norms', 'dense'; '' = none)")
+                         "('norms', 'dense', 'pack'; '' = none)")
     ap.add_argument("--only-extras", action="store_true",
                     help="measure only the extras and print them as one JSON line (profiling)")
     ap.add_argument("--calib-mib", type=int, default=0,
@@ -301,6 +347,8 @@ def main():
             ext["rmsnorm"] = measure_norms(max(args.steps // 2, 5))
         if "dense" in extras_req:
             ext["dense_block"] = measure_dense(max(args.steps // 2, 5))
+        if "pack" in extras_req:
+            ext["expert_pack"] = measure_pack(max(args.steps // 2, 5))
         return ext
 
     if args.only_extras:

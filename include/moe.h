@@ -153,6 +153,30 @@ MOE_API moe_status_t moe_dense_block_forward(moe_plan_t plan, void* workspace, s
                                              const void* norm_w, const void* gate, const void* up,
                                              const void* down, void* out);
 
+/* Expert weight layout conversion ("nemo_automodel ... glm4_moe.state_dict_adapter",
+ * Glm4MoeStateDictAdapter: HF checkpoints keep each expert's gate_proj, up_proj and
+ * down_proj as separate nn.Linear weights; the native grouped layout stacks them
+ * as gate_and_up_projs [n_experts, dim, 2*moe_inter_dim] and down_projs
+ * [n_experts, moe_inter_dim, dim]).  One expert per call (d = dim, I = inter):
+ *
+ *   moe_pack_expert:   gate [I, d], up [I, d], down [d, I]   (HF, nn.Linear [out, in])
+ *                      -> gate_up [d, 2I]: gate_up[i][n] = gate[n][i], gate_up[i][I+n] = up[n][i]
+ *                         down_packed [I, d]: down_packed[n][m] = down[m][n]
+ *   moe_unpack_expert: the inverse.
+ *
+ * gate_up / down_packed are expert e's slices of the grouped tensors
+ * (gate_and_up_projs + e*d*2I, down_projs + e*I*d elements).  Bits are moved, not
+ * converted.  dtype is moe_dtype_t; dim and inter are multiples of 64
+ * (NOT_SUPPORTED otherwise); pointers are 16-byte aligned device memory
+ * (MISALIGNED); no output may overlap an input or another output
+ * (INVALID_VALUE).  Enqueued on `stream`; returns asynchronously. */
+MOE_API moe_status_t moe_pack_expert(void* stream, int32_t dtype, int32_t dim, int32_t inter,
+                                     const void* gate, const void* up, const void* down,
+                                     void* gate_up, void* down_packed);
+MOE_API moe_status_t moe_unpack_expert(void* stream, int32_t dtype, int32_t dim, int32_t inter,
+                                       const void* gate_up, const void* down_packed, void* gate,
+                                       void* up, void* down);
+
 /* Copy the routing of the last forward call that used `workspace` into caller
  * buffers (device memory), enqueued on `stream`:
  *   topk_idx [num_tokens, top_k] int32  experts in (key desc, index asc) order

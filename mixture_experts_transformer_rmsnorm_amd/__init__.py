@@ -36,7 +36,7 @@ ABI_VERSION = 1
 EXPORTS = ("moe_plan_create", "moe_plan_destroy", "moe_block_forward", "moe_read_routing",
            "moe_read_buffer", "moe_buffer_bytes", "moe_plan_path", "moe_set_stage_timing",
            "moe_stage_times", "moe_stage_name", "moe_status_string", "moe_abi_version",
-           "moe_rmsnorm", "moe_dense_block_forward")
+           "moe_rmsnorm", "moe_dense_block_forward", "moe_pack_expert", "moe_unpack_expert")
 
 
 class MoEError(RuntimeError):
@@ -91,11 +91,13 @@ def load(path: str = LIB_PATH):
         lib.moe_status_string.restype = ctypes.c_char_p
         lib.moe_rmsnorm.argtypes = [P, i32, i64, i32, ctypes.c_float, P, i64, P, P, i64]
         lib.moe_dense_block_forward.argtypes = [P, P, ctypes.c_size_t, P, i64, P, P, P, P, P, P]
+        lib.moe_pack_expert.argtypes = [P, i32, i32, i32, P, P, P, P, P]
+        lib.moe_unpack_expert.argtypes = [P, i32, i32, i32, P, P, P, P, P]
         lib.moe_abi_version.argtypes = []
         lib.moe_abi_version.restype = i32
         for fn in ("moe_plan_create", "moe_plan_destroy", "moe_block_forward", "moe_read_routing",
                    "moe_read_buffer", "moe_set_stage_timing", "moe_stage_times", "moe_rmsnorm",
-                   "moe_dense_block_forward"):
+                   "moe_dense_block_forward", "moe_pack_expert", "moe_unpack_expert"):
             getattr(lib, fn).restype = i32
         if lib.moe_abi_version() != ABI_VERSION:
             raise ImportError("libmoe_mi355x.so ABI %d != binding ABI %d"
@@ -202,6 +204,33 @@ def moe_dense_block_forward(plan, workspace, workspace_bytes, stream, num_tokens
     _check(load().moe_dense_block_forward(plan, _ptr(workspace), workspace_bytes, _stream(stream),
                                           num_tokens, _ptr(x), _ptr(norm_w), _ptr(gate), _ptr(up),
                                           _ptr(down), _ptr(out)), "moe_dense_block_forward")
+
+
+def moe_pack_expert(stream, dtype, dim, inter, gate, up, down, gate_up, down_packed) -> None:
+    _check(load().moe_pack_expert(_stream(stream), dtype, dim, inter, _ptr(gate), _ptr(up),
+                                  _ptr(down), _ptr(gate_up), _ptr(down_packed)), "moe_pack_expert")
+
+
+def moe_unpack_expert(stream, dtype, dim, inter, gate_up, down_packed, gate, up, down) -> None:
+    _check(load().moe_unpack_expert(_stream(stream), dtype, dim, inter, _ptr(gate_up),
+                                    _ptr(down_packed), _ptr(gate), _ptr(up), _ptr(down)),
+           "moe_unpack_expert")
+
+
+def pack_experts(gates, ups, downs, gate_up=None, down=None, stream=None):
+    """HF per-expert weights (sequences of torch tensors: gate/up [I, d], down [d, I]) ->
+    grouped gate_and_up [E, d, 2I] and down [E, I, d] (allocated unless given)."""
+    import torch
+    E = len(gates)
+    I, d = gates[0].shape
+    dt = {torch.bfloat16: MOE_DTYPE_BF16, torch.float32: MOE_DTYPE_F32}[gates[0].dtype]
+    if gate_up is None:
+        gate_up = torch.empty((E, d, 2 * I), dtype=gates[0].dtype, device=gates[0].device)
+    if down is None:
+        down = torch.empty((E, I, d), dtype=gates[0].dtype, device=gates[0].device)
+    for e in range(E):
+        moe_pack_expert(stream, dt, d, I, gates[e], ups[e], downs[e], gate_up[e], down[e])
+    return gate_up, down
 
 
 def moe_read_routing(plan, workspace, stream, num_tokens, top_k, topk_idx=None, topk_w=None,

@@ -83,6 +83,19 @@ hipError_t launch_combine(int dtype, const void* x, const float* shared_part, in
                           const void* y, const float* topk_w, const int32_t* row_of, int64_t T,
                           int d, int k, void* out, hipStream_t s);
 
+// ---------------------------------------------------------------- layout conversion
+// Up to three matrices of equal element count: dst[m][c][r] = src[m][r][c] for an
+// rows[m] x cols[m] matrix (both multiples of 64); rows of src / dst are ld_src /
+// ld_dst elements apart.
+struct TransposeBatch {
+  const void* src[3];
+  void* dst[3];
+  int rows[3], cols[3];
+  int64_t ld_src[3], ld_dst[3];
+  int count;
+};
+hipError_t launch_transpose(int dtype, const TransposeBatch& b, hipStream_t s);
+
 // ---------------------------------------------------------------- routed experts
 struct GroupArgs {
   const int32_t* counts;

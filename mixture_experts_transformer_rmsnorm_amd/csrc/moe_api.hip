@@ -487,6 +487,83 @@ moe_status_t moe_dense_block_forward(moe_plan_t p, void* workspace, size_t works
   return err == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
 }
 
+namespace {
+// [p, p + bytes) and [q, q + bytes2) overlap
+bool overlaps(const void* p, size_t bytes, const void* q, size_t bytes2) {
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + bytes2 && b < a + bytes;
+}
+
+moe_status_t pack_args_ok(int32_t dtype, int32_t dim, int32_t inter, const void* const* in, int n_in,
+                          const size_t* in_bytes, void* const* out, int n_out,
+                          const size_t* out_bytes) {
+  if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16) return MOE_ERROR_NOT_SUPPORTED;
+  if (dim <= 0 || inter <= 0 || dim > (1 << 20) || inter > (1 << 20)) return MOE_ERROR_INVALID_VALUE;
+  if (dim % 64 || inter % 64) return MOE_ERROR_NOT_SUPPORTED;
+  for (int i = 0; i < n_in; ++i)
+    if (!in[i]) return MOE_ERROR_INVALID_VALUE;
+  for (int i = 0; i < n_out; ++i)
+    if (!out[i]) return MOE_ERROR_INVALID_VALUE;
+  for (int i = 0; i < n_in; ++i)
+    if (misaligned(in[i])) return MOE_ERROR_MISALIGNED;
+  for (int i = 0; i < n_out; ++i)
+    if (misaligned(out[i])) return MOE_ERROR_MISALIGNED;
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlaps(out[i], out_bytes[i], in[j], in_bytes[j])) return MOE_ERROR_INVALID_VALUE;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(out[i], out_bytes[i], out[j], out_bytes[j])) return MOE_ERROR_INVALID_VALUE;
+  }
+  return MOE_SUCCESS;
+}
+}  // namespace
+
+moe_status_t moe_pack_expert(void* stream, int32_t dtype, int32_t dim, int32_t inter,
+                             const void* gate, const void* up, const void* down, void* gate_up,
+                             void* down_packed) {
+  const size_t es = dtype == MOE_DTYPE_BF16 ? 2 : 4, n = (size_t)dim * (size_t)inter * es;
+  const void* in[3] = {gate, up, down};
+  const size_t in_b[3] = {n, n, n};
+  void* out[2] = {gate_up, down_packed};
+  const size_t out_b[2] = {2 * n, n};
+  const moe_status_t st = pack_args_ok(dtype, dim, inter, in, 3, in_b, out, 2, out_b);
+  if (st != MOE_SUCCESS) return st;
+  // gate_up[i][n] = gate[n][i], gate_up[i][I + n] = up[n][i], down_packed[n][m] = down[m][n]
+  TransposeBatch b{};
+  b.count = 3;
+  b.src[0] = gate, b.dst[0] = gate_up, b.rows[0] = inter, b.cols[0] = dim;
+  b.ld_src[0] = dim, b.ld_dst[0] = 2 * (int64_t)inter;
+  b.src[1] = up, b.dst[1] = (char*)gate_up + (size_t)inter * es, b.rows[1] = inter, b.cols[1] = dim;
+  b.ld_src[1] = dim, b.ld_dst[1] = 2 * (int64_t)inter;
+  b.src[2] = down, b.dst[2] = down_packed, b.rows[2] = dim, b.cols[2] = inter;
+  b.ld_src[2] = inter, b.ld_dst[2] = dim;
+  const hipError_t e = launch_transpose(dtype == MOE_DTYPE_BF16 ? kBF16 : kF32, b, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
+}
+
+moe_status_t moe_unpack_expert(void* stream, int32_t dtype, int32_t dim, int32_t inter,
+                               const void* gate_up, const void* down_packed, void* gate, void* up,
+                               void* down) {
+  const size_t es = dtype == MOE_DTYPE_BF16 ? 2 : 4, n = (size_t)dim * (size_t)inter * es;
+  const void* in[2] = {gate_up, down_packed};
+  const size_t in_b[2] = {2 * n, n};
+  void* out[3] = {gate, up, down};
+  const size_t out_b[3] = {n, n, n};
+  const moe_status_t st = pack_args_ok(dtype, dim, inter, in, 2, in_b, out, 3, out_b);
+  if (st != MOE_SUCCESS) return st;
+  // gate[n][i] = gate_up[i][n], up[n][i] = gate_up[i][I + n], down[m][n] = down_packed[n][m]
+  TransposeBatch b{};
+  b.count = 3;
+  b.src[0] = gate_up, b.dst[0] = gate, b.rows[0] = dim, b.cols[0] = inter;
+  b.ld_src[0] = 2 * (int64_t)inter, b.ld_dst[0] = dim;
+  b.src[1] = (const char*)gate_up + (size_t)inter * es, b.dst[1] = up, b.rows[1] = dim;
+  b.cols[1] = inter, b.ld_src[1] = 2 * (int64_t)inter, b.ld_dst[1] = dim;
+  b.src[2] = down_packed, b.dst[2] = down, b.rows[2] = inter, b.cols[2] = dim;
+  b.ld_src[2] = dim, b.ld_dst[2] = inter;
+  const hipError_t e = launch_transpose(dtype == MOE_DTYPE_BF16 ? kBF16 : kF32, b, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
+}
+
 size_t moe_buffer_bytes(moe_plan_t p, int64_t T, int32_t k, int32_t which) {
   if (!p || T < 0 || T > p->cfg.max_tokens) return 0;
   const moe_config_t& c = p->cfg;

@@ -223,3 +223,33 @@ def test_dense_plan_entry_points_and_buffers():
     finally:
         moe.moe_plan_destroy(plan)
         moe.moe_plan_destroy(moe_plan)
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(dtype=5), moe.MOE_ERROR_NOT_SUPPORTED),
+    (dict(dim=100), moe.MOE_ERROR_NOT_SUPPORTED),
+    (dict(inter=0), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(gate=None), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(gate=0x100008), moe.MOE_ERROR_MISALIGNED),
+    (dict(gate_up=0x100000 + 4096), moe.MOE_ERROR_INVALID_VALUE),  # output overlaps input gate
+    (dict(down_packed=0x600000 + 16), moe.MOE_ERROR_INVALID_VALUE),  # outputs overlap
+])
+def test_pack_validation(args, status):
+    a = dict(dtype=moe.MOE_DTYPE_BF16, dim=256, inter=128, gate=0x100000, up=0x200000,
+             down=0x300000, gate_up=0x600000, down_packed=0x700000)
+    a.update(args)
+    got = moe.load().moe_pack_expert(0, a["dtype"], a["dim"], a["inter"], a["gate"], a["up"],
+                                     a["down"], a["gate_up"], a["down_packed"])
+    assert got == status
+    if "gate_up" not in args and "down_packed" not in args:
+        # shape, dtype and pointer checks are the same in the inverse direction
+        got = moe.load().moe_unpack_expert(0, a["dtype"], a["dim"], a["inter"], a["gate_up"],
+                                           a["down_packed"], a["gate"], a["up"], a["down"])
+        assert got == status
+
+
+def test_unpack_rejects_outputs_overlapping_inputs():
+    lib = moe.load()
+    # output `up` inside the input gate_up
+    assert lib.moe_unpack_expert(0, moe.MOE_DTYPE_BF16, 256, 128, 0x600000, 0x700000, 0x100000,
+                                 0x600000 + 1024, 0x300000) == moe.MOE_ERROR_INVALID_VALUE
