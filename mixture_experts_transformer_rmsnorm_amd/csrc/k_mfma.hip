@@ -30,12 +30,11 @@
 #include <type_traits>
 
 #include "common.h"
+#include "dev_nt.h"
 #include "kernels.h"
 
 namespace moe {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
@@ -76,112 +75,11 @@ struct MfmaProblem {
 };
 
 // ---------------------------------------------------------------------------
-// Dense kernel
-constexpr int BM = kMfmaBM, BN = kMfmaBN, BK = kMfmaBK;
-constexpr int LDK = BK + 8;  // K-contiguous LDS rows: 72 elements (144 bytes)
-constexpr int kTileElems = BM * LDK;
-
-// B-columns of wave column wn: [wn*32, wn*32+32) (f = 0) and [64+wn*32, 64+wn*32+32) (f = 1)
-__device__ __forceinline__ int b_local_col(int f, int wn) { return f * 64 + wn * 32; }
-
-__global__ __launch_bounds__(256) void mfma_nt_kernel(MfmaProblem p) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2 * kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2 * kTileElems];
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const int n_tile = blockIdx.x;
-  const int m0 = blockIdx.y * BM;
-  const int rows = min(BM, p.M - m0);
-  const int nkt = p.K / BK;
-  const int kt0 = blockIdx.z * p.kt_per_split;
-  const int kt1 = min(nkt, kt0 + p.kt_per_split);
-
-  // ---- per-thread global load assignments: A rows and B rows tid/8 + 32*i,
-  // 16-byte chunk tid%8.  Rows past the tile's valid rows (and B rows past N)
-  // load a valid row instead: they only feed outputs the epilogue never
-  // stores, and unconditional loads keep the wait counts of the pipeline exact.
-  const uint16_t* a_src[4];
-  const uint16_t* b_src[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = min(tid / 8 + 32 * i, rows - 1);
-    a_src[i] = p.A + (int64_t)(m0 + r) * p.lda + (tid % 8) * 8;
-    const int n = n_tile * BN + tid / 8 + 32 * i;
-    const int nn = n < p.N ? n : 0;
-    const uint16_t* row = nn < p.n_split ? p.B1 + (int64_t)nn * p.ldb
-                                         : p.B2 + (int64_t)(nn - p.n_split) * p.ldb;
-    b_src[i] = row + (tid % 8) * 8;
-  }
-
-  uint4 ra[4], rb[4];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = ldg16(a_src[i] + k0);
-      rb[i] = ldg16(b_src[i] + k0);
-    }
-  };
-  auto lstore = [&](int buf) {
-    uint16_t* as = As + buf * kTileElems;
-    uint16_t* bs = Bs + buf * kTileElems;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4*>(as + (tid / 8 + 32 * i) * LDK + (tid % 8) * 8) = ra[i];
-      *reinterpret_cast<uint4*>(bs + (tid / 8 + 32 * i) * LDK + (tid % 8) * 8) = rb[i];
-    }
-  };
-
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
-
-  if (kt0 < kt1) {
-    gload(kt0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = kt0; kt < kt1; ++kt) {
-      const int buf = (kt - kt0) & 1;
-      if (kt + 1 < kt1) gload(kt + 1);
-      const uint16_t* as = As + buf * kTileElems;
-      const uint16_t* bs = Bs + buf * kTileElems;
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int kof = ks * 16 + (lane >> 5) * 8;
-        bf16x8_t af[2], bf[2];
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-          af[mi] = *reinterpret_cast<const bf16x8_t*>(as + (wm * 64 + mi * 32 + (lane & 31)) * LDK + kof);
-#pragma unroll
-        for (int f = 0; f < 2; ++f)
-          bf[f] = *reinterpret_cast<const bf16x8_t*>(bs + (b_local_col(f, wn) + (lane & 31)) * LDK + kof);
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-          for (int f = 0; f < 2; ++f)
-            acc[mi][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[f], acc[mi][f], 0, 0, 0);
-      }
-      if (kt + 1 < kt1) lstore(buf ^ 1);
-      __syncthreads();
-    }
-  }
-
-  const int col32 = lane & 31;
-  float* out = (float*)p.C + (int64_t)blockIdx.z * p.M * p.N;
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const int n = n_tile * BN + b_local_col(f, wn) + col32;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (r < rows && n < p.N) out[(int64_t)(m0 + r) * p.N + n] = acc[mi][f][i];
-      }
-    }
+// Dense kernel for fewer rows (mfma_nt_kernel): one 128 x 128 tile per block
+// (nt_tile_128, in dev_nt.h).
+__global__ __launch_bounds__(256) void mfma_nt_kernel(NtArgs a) {
+  __shared__ __attribute__((aligned(16))) NtSmem sm;
+  nt_tile_128(a, blockIdx.x, blockIdx.y, blockIdx.z, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -653,8 +551,8 @@ hipError_t launch_mfma_nt(const NtArgs& a, hipStream_t s) {
     const int64_t blocks = (tiles + kXcds - 1) / kXcds * kXcds;
     mfma_nt_big_kernel<<<dim3((unsigned)blocks), NB_THREADS, 0, s>>>(p);
   } else {
-    dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, a.splits);
-    mfma_nt_kernel<<<grid, 256, 0, s>>>(p);
+    dim3 grid((a.N + kNtBN - 1) / kNtBN, (a.M + kNtBM - 1) / kNtBM, a.splits);
+    mfma_nt_kernel<<<grid, 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }
