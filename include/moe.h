@@ -88,8 +88,15 @@ typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
  *          batches, where the expert weights are streamed once from HBM), MFMA
  *          otherwise.  fp32 plans always use STREAM.
  *  STREAM: weight-streaming FMA kernels (any dtype).
- *  MFMA:   LDS-tiled bf16 matrix-core kernels (bf16 only). */
-typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_MFMA = 2 } moe_path_t;
+ *  MFMA:   LDS-tiled bf16 matrix-core kernels (bf16 only).
+ *  FUSED:  reserved for a single persistent decode kernel; not available in this
+ *          build (moe_plan_create returns NOT_SUPPORTED). */
+typedef enum {
+  MOE_PATH_AUTO = 0,
+  MOE_PATH_STREAM = 1,
+  MOE_PATH_MFMA = 2,
+  MOE_PATH_FUSED = 3
+} moe_path_t;
 
 typedef struct {
   uint32_t struct_size;  /* sizeof(moe_config_t) */
@@ -223,7 +230,9 @@ typedef enum {
   MOE_BUF_ACT = 4,        /* [T*k, I] D: silu(gate) * up per permuted row */
   MOE_BUF_Y = 5,          /* [T*k, d] D: routed expert output per permuted row */
   MOE_BUF_SHARED_ACT = 6, /* [T, Is] D: shared expert silu(gate) * up */
-  MOE_BUF_COUNT = 7
+  MOE_BUF_FUSED_ERROR = 7, /* [1] uint32: error word of the fused decode kernel (reserved;
+                              0 while that kernel is not available) */
+  MOE_BUF_COUNT = 8
 } moe_buffer_t;
 
 /* Copy intermediate buffer `which` of the last forward call into `dst` (device
@@ -235,7 +244,8 @@ MOE_API moe_status_t moe_read_buffer(moe_plan_t plan, const void* workspace, voi
 /* Size in bytes of intermediate buffer `which` for num_tokens/top_k (0 if invalid). */
 MOE_API size_t moe_buffer_bytes(moe_plan_t plan, int64_t num_tokens, int32_t top_k, int32_t which);
 
-/* Path the plan takes for num_tokens/top_k (MOE_PATH_STREAM or MOE_PATH_MFMA); for
+/* Path the plan takes for num_tokens/top_k (MOE_PATH_STREAM, MOE_PATH_MFMA or
+ * MOE_PATH_FUSED); for
  * a dense-block plan, MFMA for bf16 and STREAM (the fp32 FMA products) for fp32. */
 MOE_API int32_t moe_plan_path(moe_plan_t plan, int64_t num_tokens, int32_t top_k);
 

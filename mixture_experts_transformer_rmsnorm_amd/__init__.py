@@ -27,9 +27,9 @@ MOE_ERROR_WORKSPACE_TOO_SMALL = 3
 MOE_ERROR_MISALIGNED = 4
 MOE_ERROR_HIP = 5
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
-MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_MFMA = 0, 1, 2
+MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_MFMA, MOE_PATH_FUSED = 0, 1, 2, 3
 (MOE_BUF_H, MOE_BUF_OFFSETS, MOE_BUF_PERM_TOKEN, MOE_BUF_ROW_OF, MOE_BUF_ACT, MOE_BUF_Y,
- MOE_BUF_SHARED_ACT) = range(7)
+ MOE_BUF_SHARED_ACT, MOE_BUF_FUSED_ERROR) = range(8)
 MOE_MAX_STAGES = 16
 ABI_VERSION = 1
 
@@ -344,6 +344,11 @@ class MoEBlock:
         cnt = torch.empty((self.n_experts,), dtype=torch.int32, device=dev)
         moe_read_routing(self.plan, self.workspace, stream, num_tokens, self.top_k, idx, wts, cnt)
         return idx, wts, cnt
+
+    def fused_error(self, num_tokens, stream=None) -> int:
+        """The fused decode kernel's error word of the last call (0 = every wait completed)."""
+        import numpy as np
+        return int(self.buffer(MOE_BUF_FUSED_ERROR, num_tokens, stream).cpu().numpy().view(np.uint32)[0])
 
     def buffer(self, which, num_tokens, stream=None):
         """Intermediate buffer `which` (MOE_BUF_*) of the last call as a flat uint8 tensor."""

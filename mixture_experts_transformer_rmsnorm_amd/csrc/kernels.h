@@ -119,4 +119,57 @@ hipError_t launch_mfma_gate_up(const GroupArgs& g, int max_mtiles, const void* h
 hipError_t launch_mfma_down(const GroupArgs& g, int max_mtiles, const void* act, const void* down,
                             void* y, hipStream_t s);
 
+// ---------------------------------------------------------------- fused decode
+// Phases of the fused decode kernel, in the order its items are handed out; every
+// phase depends only on earlier ones.
+enum FusedPhase {
+  kPhNorm = 0, kPhRouter, kPhTopk, kPhScan, kPhScatter, kPhShGu, kPhGu, kPhShAct, kPhShDn, kPhDn,
+  kPhCombine, kFusedPhases
+};
+// Words of the fused kernel's synchronisation state: ticket, error flag, one done
+// counter per phase, one per expert (its gate/up items).
+inline int kFusedSyncWords(int E) { return 2 + kFusedPhases + E; }
+
+struct bf16;
+struct FusedArgs {
+  const bf16* x;
+  const bf16* norm_w;
+  const bf16* router_w;
+  const float* corr_bias;
+  const bf16* gate_up;
+  const bf16* down;
+  const bf16* sg;
+  const bf16* su;
+  const bf16* sd;
+  bf16* out;
+  int64_t T;
+  int d, E, I, Is, k;
+  float eps, rs;
+  // workspace buffers (the layouts of the multi-kernel path)
+  bf16* h;
+  float* logits;
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* chunk_cnt;
+  int32_t* counts;
+  int32_t* offsets;
+  RouteHeader* hdr;
+  int32_t* active;
+  int32_t* perm_token;
+  int32_t* row_of;
+  bf16* act;
+  bf16* y;
+  float* sh_gu;
+  bf16* act_s;
+  float* sh_dn;
+  // split-K of the router and shared-expert products
+  int r_splits, r_kper, sg_splits, sg_kper, sd_splits, sd_kper;
+  uint32_t* sync;                // kFusedSyncWords(E) words
+  int start[kFusedPhases + 1];   // first item of each phase (set by the launcher)
+};
+// Items of each phase; returns the total.
+int fused_item_counts(const FusedArgs& f, int* counts);
+// Resets the synchronisation state, then runs the persistent kernel on `grid` blocks.
+hipError_t launch_fused_decode(FusedArgs f, int grid, hipStream_t s);
+
 }  // namespace moe

@@ -42,12 +42,15 @@ enum Stage {
   kStDown,
   kStSharedDown,
   kStCombine,
+  kStFused,  // the whole forward in the fused decode kernel
   kNumStages
 };
 const char* const kStageNames[kNumStages] = {
     "rmsnorm",       "router_logits",   "router_topk", "permute_scan", "permute_scatter",
     "expert_gate_up", "shared_gate_up", "shared_act",  "expert_down",  "shared_down",
-    "combine"};
+    "combine",        "fused_decode"};
+// Largest batch the fused decode kernel takes.
+constexpr int64_t kFusedMaxTokens = 64;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -72,7 +75,7 @@ Split nt_split(int64_t M, int64_t N, int64_t K, int tm, int tn, int tk, int max_
 
 struct Layout {
   size_t h, logits, topk_idx, topk_w, chunk_cnt, counts, offsets, hdr, active, mtiles,
-      perm_token, row_of, act, y, sh_gu, act_s, sh_dn, total;
+      perm_token, row_of, act, y, sh_gu, act_s, sh_dn, sync, total;
 };
 
 struct EventPair {
@@ -101,6 +104,19 @@ bool use_mfma(const moe_plan* p, int64_t T, int k) {
   if (p->cfg.path == MOE_PATH_STREAM) return false;
   if (p->cfg.path == MOE_PATH_MFMA) return true;
   return T * k > (int64_t)kStreamMaxMeanTokens * p->cfg.n_experts;
+}
+
+// The fused decode kernel: bf16 MoE plans, at most kFusedMaxTokens tokens, under
+// MOE_PATH_FUSED or (AUTO) whenever the streaming kernels would be chosen.
+// The fused decode kernel is switched off: its first run on the GPU did not finish
+// and the cause has not been established, so no plan reaches it (plan creation
+// rejects MOE_PATH_FUSED and AUTO never picks it).
+constexpr bool kFusedEnabled = false;
+bool use_fused(const moe_plan* p, int64_t T, int k) {
+  if (!kFusedEnabled) return false;
+  if (p->cfg.dtype != MOE_DTYPE_BF16 || p->cfg.n_experts == 0 || T > kFusedMaxTokens) return false;
+  if (p->cfg.path == MOE_PATH_FUSED) return true;
+  return p->cfg.path == MOE_PATH_AUTO && !use_mfma(p, T, k);
 }
 
 // Tile sizes of the dense K-contiguous products of T rows for this plan's dtype.
@@ -162,6 +178,7 @@ void make_layout(moe_plan* p) {
   } else {
     L.sh_gu = L.act_s = L.sh_dn = 0;
   }
+  L.sync = take((size_t)kFusedSyncWords(std::max(c.n_experts, 1)) * 4);
   L.total = off;
 }
 
@@ -214,8 +231,10 @@ moe_status_t moe_plan_create(const moe_config_t* cfg, moe_plan_t* plan, size_t* 
             : (cfg->moe_inter <= 0 || cfg->max_top_k < 1 || cfg->max_top_k > cfg->n_experts))
     return MOE_ERROR_INVALID_VALUE;
   if (cfg->dtype != MOE_DTYPE_F32 && cfg->dtype != MOE_DTYPE_BF16) return MOE_ERROR_NOT_SUPPORTED;
-  if (cfg->path < MOE_PATH_AUTO || cfg->path > MOE_PATH_MFMA) return MOE_ERROR_INVALID_VALUE;
-  if (cfg->path == MOE_PATH_MFMA && cfg->dtype != MOE_DTYPE_BF16) return MOE_ERROR_NOT_SUPPORTED;
+  if (cfg->path < MOE_PATH_AUTO || cfg->path > MOE_PATH_FUSED) return MOE_ERROR_INVALID_VALUE;
+  if ((cfg->path == MOE_PATH_MFMA || cfg->path == MOE_PATH_FUSED) && cfg->dtype != MOE_DTYPE_BF16)
+    return MOE_ERROR_NOT_SUPPORTED;
+  if (cfg->path == MOE_PATH_FUSED && !kFusedEnabled) return MOE_ERROR_NOT_SUPPORTED;
   if (cfg->dim % 64 || cfg->moe_inter % 64 || cfg->shared_inter % 64 ||
       cfg->n_experts > kMaxExperts || cfg->max_top_k > kMaxTopK)
     return MOE_ERROR_NOT_SUPPORTED;
@@ -247,6 +266,7 @@ int32_t moe_plan_path(moe_plan_t p, int64_t num_tokens, int32_t top_k) {
   if (!p) return -1;
   if (p->cfg.n_experts == 0)  // dense plan: the family of its K-contiguous products
     return p->cfg.dtype == MOE_DTYPE_BF16 ? MOE_PATH_MFMA : MOE_PATH_STREAM;
+  if (use_fused(p, num_tokens, top_k)) return MOE_PATH_FUSED;
   return use_mfma(p, num_tokens, top_k) ? MOE_PATH_MFMA : MOE_PATH_STREAM;
 }
 
@@ -372,6 +392,28 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   const Split sgsplit =
       has_shared ? nt_split(T, 2 * (int64_t)Is, d, tm, tn, tk, kMaxSharedSplits) : Split{0, 0};
 
+  if (use_fused(p, T, k)) {
+    FusedArgs f{};
+    f.x = (const bf16*)x, f.norm_w = (const bf16*)norm_w, f.router_w = (const bf16*)router_w;
+    f.corr_bias = corr_bias, f.gate_up = (const bf16*)gate_up, f.down = (const bf16*)down;
+    f.sg = (const bf16*)shared_gate, f.su = (const bf16*)shared_up, f.sd = (const bf16*)shared_down;
+    f.out = (bf16*)out;
+    f.T = T, f.d = d, f.E = E, f.I = I, f.Is = Is, f.k = k, f.eps = c.eps, f.rs = routed_scale;
+    f.h = (bf16*)h, f.logits = logits, f.topk_idx = topk_idx, f.topk_w = topk_w;
+    f.chunk_cnt = chunk_cnt, f.counts = counts, f.offsets = offsets, f.hdr = hdr, f.active = active;
+    f.perm_token = perm_token, f.row_of = row_of, f.act = (bf16*)act, f.y = (bf16*)y;
+    f.sh_gu = sh_gu, f.act_s = (bf16*)act_s, f.sh_dn = sh_dn;
+    f.r_splits = rsplit.splits, f.r_kper = rsplit.kt_per;
+    f.sg_splits = sgsplit.splits, f.sg_kper = sgsplit.kt_per;
+    f.sd_splits = sdsplit.splits, f.sd_kper = sdsplit.kt_per;
+    f.sync = (uint32_t*)(ws + L.sync);
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return MOE_ERROR_HIP;
+    stage(kStFused, [&] { return launch_fused_decode(f, 2 * std::max(cus, 1), s); });
+    return err == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
+  }
   stage(kStNorm, [&] { return launch_rmsnorm(dt, x, d, norm_w, h, d, T, d, c.eps, s); });
   stage(kStRouter,
         [&] { return nt(h, d, router_w, router_w, d, E, logits, E, d, kMaxRouterSplits); });
@@ -583,6 +625,7 @@ size_t moe_buffer_bytes(moe_plan_t p, int64_t T, int32_t k, int32_t which) {
     case MOE_BUF_ACT: return (size_t)A * c.moe_inter * p->es;
     case MOE_BUF_Y: return (size_t)A * c.dim * p->es;
     case MOE_BUF_SHARED_ACT: return (size_t)T * c.shared_inter * p->es;
+    case MOE_BUF_FUSED_ERROR: return 4;
   }
   return 0;
 }
@@ -633,6 +676,7 @@ moe_status_t moe_read_buffer(moe_plan_t p, const void* workspace, void* stream, 
     case MOE_BUF_ACT: off = L.act; break;
     case MOE_BUF_Y: off = L.y; break;
     case MOE_BUF_SHARED_ACT: off = L.act_s; break;
+    case MOE_BUF_FUSED_ERROR: off = L.sync + 4; break;
   }
   const hipError_t e = hipMemcpyAsync(dst, (const char*)workspace + off, bytes,
                                       hipMemcpyDeviceToDevice, (hipStream_t)stream);

@@ -53,6 +53,8 @@ def _cfg(**kw):
     (dict(dtype=7), moe.MOE_ERROR_NOT_SUPPORTED),
     (dict(dtype="f32", path=moe.MOE_PATH_MFMA), moe.MOE_ERROR_NOT_SUPPORTED),
     (dict(path=5), moe.MOE_ERROR_INVALID_VALUE),
+    (dict(dtype="f32", path=moe.MOE_PATH_FUSED), moe.MOE_ERROR_NOT_SUPPORTED),
+    (dict(path=moe.MOE_PATH_FUSED), moe.MOE_ERROR_NOT_SUPPORTED),   # switched off in this build
     (dict(flags=1), moe.MOE_ERROR_INVALID_VALUE),
 ])
 def test_plan_validation(kw, status):

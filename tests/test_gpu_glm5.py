@@ -95,13 +95,22 @@ def _check(cfg, weights, path=moe.MOE_PATH_AUTO, n_sample=None):
                                     dn, sh[0], sh[1], sh[2], oracle.DTYPES[cfg.dtype])
     got = workloads.torch_to_host(out)[tokens]
     check_outputs(cfg, small, got, delta, out_ref, tokens)
+    if moe.moe_plan_path(block.plan, cfg.T, cfg.k) == moe.MOE_PATH_FUSED:
+        assert block.fused_error(cfg.T) == 0
     del block
     return g
 
 
 def test_glm5_decode_stream(glm5_weights):
     cfg = workloads.config("glm5_decode")
-    _check(cfg, glm5_weights)
+    _check(cfg, glm5_weights, path=moe.MOE_PATH_STREAM)
+
+
+@pytest.mark.skip(reason="the fused decode kernel is switched off: its first GPU run did not "
+                         "finish and the cause has not been established")
+def test_glm5_decode_fused(glm5_weights):
+    cfg = workloads.config("glm5_decode")
+    _check(cfg, glm5_weights, path=moe.MOE_PATH_FUSED)
 
 
 def test_glm5_decode_mfma(glm5_weights):

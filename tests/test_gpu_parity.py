@@ -13,7 +13,7 @@ from tests.gpu_harness import (check_close, check_intermediate, check_outputs, c
 
 pytestmark = pytest.mark.gpu
 
-STREAM, MFMA = moe.MOE_PATH_STREAM, moe.MOE_PATH_MFMA
+STREAM, MFMA, FUSED = moe.MOE_PATH_STREAM, moe.MOE_PATH_MFMA, moe.MOE_PATH_FUSED
 
 
 def _full_check(cfg, small, route, tin, path, check_stages=True):
@@ -113,5 +113,49 @@ def test_smaller_call_after_larger_reuses_workspace():
     sub = dict(route, idx=route["idx"][:T2], w=route["w"][:T2], h=route["h"][:T2])
     cnt = np.bincount(sub["idx"].ravel(), minlength=cfg.E)
     assert np.array_equal(g["counts"], cnt)
+    delta, out_ref = oracle_outputs(cfg, small, route, tin, np.arange(T2))
+    check_outputs(cfg, small, workloads.torch_to_host(out), delta, out_ref, np.arange(T2))
+
+
+# ----------------------------------------------------------------------------- fused decode
+FUSED_OFF = ("the fused decode kernel is switched off: its first GPU run (case T=64 d=256 E=16 "
+             "I=192 Is=128 k=4) did not finish and the cause has not been established")
+
+
+@pytest.mark.skip(reason=FUSED_OFF)
+@pytest.mark.parametrize("shape", [
+    dict(T=64, d=256, E=16, I=192, Is=128, k=4),           # several slices per expert
+    dict(T=37, d=384, E=8, I=64, Is=192, k=2),              # odd T: a partial chunk
+    dict(T=50, d=512, E=32, I=320, Is=0, k=6, routed_scale=2.5),  # no shared expert
+    dict(T=64, d=256, E=8, I=128, Is=64, k=8),              # every expert selected
+    dict(T=40, d=256, E=300, I=128, Is=128, k=8),           # E not a multiple of 64
+    dict(T=1, d=256, E=64, I=128, Is=128, k=2),             # one token, most experts empty
+])
+def test_fused_decode(shape):
+    cfg = workloads.config("tiny_fp32", dtype="bf16", **shape)
+    cfg, small, route, tin = prepare(cfg, seed=13)
+    block, _ = _full_check(cfg, small, route, tin, FUSED)
+    assert moe.moe_plan_path(block.plan, cfg.T, cfg.k) == FUSED
+    assert block.fused_error(cfg.T) == 0
+
+
+@pytest.mark.skip(reason=FUSED_OFF)
+def test_fused_repeatability_in_place_and_workspace_reuse():
+    cfg, small, route, tin = prepare(workloads.config("tiny_fp32", dtype="bf16", T=64, E=16,
+                                                      k=4, d=256, I=128, Is=128), seed=17)
+    block, out1 = run_gpu(cfg, tin, FUSED)
+    _, out2 = run_gpu(cfg, tin, FUSED, block=block)
+    assert torch.equal(out1, out2), "bitwise repeatability"
+    xin = tin["x"].clone()
+    block.forward(xin, out=xin)  # in place
+    torch.cuda.synchronize()
+    assert torch.equal(xin, out1)
+    # the fused and the multi-kernel streaming paths compute the same thing
+    _, o_stream = run_gpu(cfg, tin, STREAM)
+    check_close(out1.float().cpu().numpy(), o_stream.float().cpu().numpy(), "bf16", "fused-vs-stream")
+    # a smaller call after a larger one on the same workspace
+    T2 = 23
+    _, out = run_gpu(cfg, tin, FUSED, T=T2, block=block)
+    assert block.fused_error(T2) == 0
     delta, out_ref = oracle_outputs(cfg, small, route, tin, np.arange(T2))
     check_outputs(cfg, small, workloads.torch_to_host(out), delta, out_ref, np.arange(T2))
