@@ -8,7 +8,6 @@
 namespace moe {
 
 constexpr int kStreamThreads = 256;
-constexpr int kStreamMaxMT = 8;  // tokens of one expert processed per pass over its weights
 
 template <typename T, int CL, bool GU>
 struct StreamShape {
@@ -18,31 +17,33 @@ struct StreamShape {
   static constexpr int RED_COLS = CL * V;                  // LDS columns per (rg, m)
 };
 
-// One pass over the slice's weights for tokens [m0, m0 + mt) of the expert
-// (mt <= MT).  Rows beyond mt repeat the last valid row and are never stored.
-template <typename T, int CL, bool GU, int MT>
-__device__ __forceinline__ void stream_pass(const GroupArgs& g, const T* __restrict__ A,
-                                            int64_t lda, const T* __restrict__ W, int64_t ldw,
-                                            int K, int n_out, int seg, int m0, int mt, int slice,
-                                            T* __restrict__ out, int64_t ldo, float* red) {
+// Columns of this lane: its 16-byte vector sits at `pos` of the slice's LDS row
+// and at column `wcol` of the weight matrix; lanes past the output width idle.
+template <typename T, int CL, bool GU>
+__device__ __forceinline__ bool stream_lane(const GroupArgs& g, int n_out, int slice, int cl,
+                                            int* pos, int* wcol) {
   using S = StreamShape<T, CL, GU>;
-  constexpr int V = S::V, RG = S::RG, SW = S::SW;
-  const int tid = threadIdx.x, cl = tid % CL, rg = tid / CL;
-
-  int pos, wcol;
-  bool lane_ok;
   if (GU) {
     const int half = cl / (CL / 2);
-    const int j = (cl % (CL / 2)) * V;
-    pos = half * SW + j;
-    wcol = (half ? g.I : 0) + slice * SW + j;
-    lane_ok = slice * SW + j < g.I;
-  } else {
-    pos = cl * V;
-    wcol = slice * SW + pos;
-    lane_ok = wcol < n_out;
+    const int j = (cl % (CL / 2)) * S::V;
+    *pos = half * S::SW + j;
+    *wcol = (half ? g.I : 0) + slice * S::SW + j;
+    return slice * S::SW + j < g.I;
   }
+  *pos = cl * S::V;
+  *wcol = slice * S::SW + *pos;
+  return *wcol < n_out;
+}
 
+// Sums over rows [kb, ke) of W: acc[m][c] += A[row m][k] * W[k][wcol + c].  Rows
+// of A beyond mt repeat the last valid row (their sums are never stored).
+template <typename T, int CL, bool GU, int MT>
+__device__ __forceinline__ void stream_accumulate(const GroupArgs& g, const T* __restrict__ A,
+                                                  int64_t lda, const T* __restrict__ W,
+                                                  int64_t ldw, int wcol, int seg, int m0, int mt,
+                                                  int kb, int ke,
+                                                  float (&acc)[MT][Elem<T>::kVec]) {
+  constexpr int V = Elem<T>::kVec;
   const T* arow[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
@@ -51,73 +52,102 @@ __device__ __forceinline__ void stream_pass(const GroupArgs& g, const T* __restr
     const int64_t r = GU ? (int64_t)g.perm_token[prow] : prow;
     arow[m] = A + r * lda;
   }
-
-  float acc[MT][V];
+  const T* wp = W + (int64_t)kb * ldw + wcol;
+  for (int k = kb; k < ke; k += V, wp += (int64_t)V * ldw) {
+    uint4 wv[V];
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+    for (int r = 0; r < V; ++r) wv[r] = ldg16_stream(wp + (int64_t)r * ldw);
+    float a[MT][V];
 #pragma unroll
-    for (int c = 0; c < V; ++c) acc[m][c] = 0.f;
-
-  const int kc = K / RG;
-  const int kb = rg * kc, ke = kb + kc;
-  if (lane_ok) {
-    const T* wp = W + (int64_t)kb * ldw + wcol;
-    for (int k = kb; k < ke; k += V, wp += (int64_t)V * ldw) {
-      uint4 wv[V];
+    for (int m = 0; m < MT; ++m) Elem<T>::unpack(ldg16(arow[m] + k), a[m]);
 #pragma unroll
-      for (int r = 0; r < V; ++r) wv[r] = ldg16_stream(wp + (int64_t)r * ldw);
-      float a[MT][V];
+    for (int r = 0; r < V; ++r) {
+      float f[V];
+      Elem<T>::unpack(wv[r], f);
 #pragma unroll
-      for (int m = 0; m < MT; ++m) Elem<T>::unpack(ldg16(arow[m] + k), a[m]);
+      for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int r = 0; r < V; ++r) {
-        float f[V];
-        Elem<T>::unpack(wv[r], f);
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int c = 0; c < V; ++c) acc[m][c] += a[m][r] * f[c];
-      }
+        for (int c = 0; c < V; ++c) acc[m][c] += a[m][r] * f[c];
     }
   }
+}
 
-  __syncthreads();  // the previous pass's output phase has finished reading red
+// Writes a row group's sums to its LDS rows: red[(rg * MT + m) * RED_COLS + pos + c].
+template <typename T, int CL, bool GU, int MT>
+__device__ __forceinline__ void stream_to_lds(const float (&acc)[MT][Elem<T>::kVec], int rg,
+                                              int pos, float* red) {
+  using S = StreamShape<T, CL, GU>;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     float* dst = red + ((int64_t)rg * MT + m) * S::RED_COLS + pos;
 #pragma unroll
-    for (int c = 0; c < V; c += 4)
+    for (int c = 0; c < S::V; c += 4)
       *reinterpret_cast<float4*>(dst + c) = make_float4(acc[m][c], acc[m][c + 1], acc[m][c + 2],
                                                         acc[m][c + 3]);
   }
-  __syncthreads();
+}
 
-  const int width = GU ? g.I : n_out;
-  for (int o = tid; o < mt * SW; o += kStreamThreads) {
+// Output phase of a slice: v = silu(gate) * up (gate_up) or the sum (down), from
+// the per-column sums in LDS rows red[m * RED_COLS + ...] (row group 0's rows).
+template <typename T, int CL, bool GU, int MT>
+__device__ __forceinline__ void stream_store(const float* red, int width, int seg, int m0, int mt,
+                                             int slice, T* __restrict__ out, int64_t ldo) {
+  using S = StreamShape<T, CL, GU>;
+  constexpr int SW = S::SW;
+  for (int o = threadIdx.x; o < mt * SW; o += kStreamThreads) {
     const int m = o / SW, j = o % SW;
     const int col = slice * SW + j;
     if (col >= width) continue;
-    float v;
-    if (GU) {
-      float gs = 0.f, us = 0.f;
-#pragma unroll
-      for (int q = 0; q < RG; ++q) {
-        const float* src = red + ((int64_t)q * MT + m) * S::RED_COLS;
-        gs += src[j];
-        us += src[SW + j];
-      }
-      v = silu(gs) * us;
-    } else {
-      v = 0.f;
-#pragma unroll
-      for (int q = 0; q < RG; ++q) v += red[((int64_t)q * MT + m) * S::RED_COLS + j];
-    }
+    const float* src = red + (int64_t)m * S::RED_COLS;
+    const float v = GU ? silu(src[j]) * src[SW + j] : src[j];
     T* dst = out + (int64_t)(seg + m0 + m) * ldo + col;
     if constexpr (sizeof(T) == 2)
       reinterpret_cast<uint16_t*>(dst)[0] = (uint16_t)f32_to_bf16_bits(v);
     else
       reinterpret_cast<float*>(dst)[0] = v;
   }
+}
+
+// Adds the RG row groups' sums of each (m, column) in a fixed order, in place into
+// row group 0's rows.  Each sum is read and written by one thread only.
+template <typename T, int CL, bool GU, int MT>
+__device__ __forceinline__ void stream_reduce_rg(float* red, int mt) {
+  using S = StreamShape<T, CL, GU>;
+  for (int o = threadIdx.x; o < mt * S::RED_COLS; o += kStreamThreads) {
+    const int m = o / S::RED_COLS, j = o % S::RED_COLS;
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < S::RG; ++q) v += red[((int64_t)q * MT + m) * S::RED_COLS + j];
+    red[(int64_t)m * S::RED_COLS + j] = v;
+  }
+}
+
+// One pass over the slice's weights for tokens [m0, m0 + mt) of the expert
+// (mt <= MT), all K rows: the row groups split K into equal contiguous ranges.
+template <typename T, int CL, bool GU, int MT>
+__device__ __forceinline__ void stream_pass(const GroupArgs& g, const T* __restrict__ A,
+                                            int64_t lda, const T* __restrict__ W, int64_t ldw,
+                                            int K, int n_out, int seg, int m0, int mt, int slice,
+                                            T* __restrict__ out, int64_t ldo, float* red) {
+  using S = StreamShape<T, CL, GU>;
+  const int tid = threadIdx.x, cl = tid % CL, rg = tid / CL;
+  int pos, wcol;
+  const bool lane_ok = stream_lane<T, CL, GU>(g, n_out, slice, cl, &pos, &wcol);
+  float acc[MT][S::V];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int c = 0; c < S::V; ++c) acc[m][c] = 0.f;
+  const int kc = K / S::RG;
+  if (lane_ok)
+    stream_accumulate<T, CL, GU, MT>(g, A, lda, W, ldw, wcol, seg, m0, mt, rg * kc, rg * kc + kc,
+                                     acc);
+  __syncthreads();  // the previous pass's output phase has finished reading red
+  stream_to_lds<T, CL, GU, MT>(acc, rg, pos, red);
+  __syncthreads();
+  stream_reduce_rg<T, CL, GU, MT>(red, mt);
+  __syncthreads();
+  stream_store<T, CL, GU, MT>(red, GU ? g.I : n_out, seg, m0, mt, slice, out, ldo);
 }
 
 // One work unit: expert e, column slice `slice`, every token routed to e (in

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256, 2) void fused_decode_kernel(FusedArgs f) {
   uint32_t* gu_done = f.sync + 2 + kFusedPhases;  // [E]
   const int total = f.start[kFusedPhases];
   const int E = f.E;
-  GroupArgs g{f.counts, f.offsets, f.hdr, f.active, nullptr, f.perm_token, f.E, f.d, f.I};
+  GroupArgs g{f.counts, f.offsets, f.hdr, f.active, nullptr, f.perm_token, nullptr, f.E, f.d, f.I};
   const int gu_slices = stream_slices<bf16, kGuCL, true>(f.I, f.d);
   const int dn_slices = stream_slices<bf16, kDnCL, false>(f.I, f.d);
 

@@ -215,34 +215,43 @@ __global__ __launch_bounds__(256) void scan_chunks_kernel(int32_t* __restrict__ 
 }
 
 // Permutation, step 2 (one block): expert segment offsets (exclusive scan of the
-// counts), the compacted list of active experts, and the M-tile work list.
+// counts), the compacted list of active experts, the M-tile work list, and the
+// first streaming pass of each active expert.
 __global__ __launch_bounds__(1024) void scan_experts_kernel(const int32_t* __restrict__ counts,
                                                             int E, int32_t* __restrict__ offsets,
                                                             RouteHeader* __restrict__ hdr,
                                                             int32_t* __restrict__ active,
-                                                            int2* __restrict__ mtiles) {
-  __shared__ int s_cnt[1024], s_act[1024], s_til[1024];
+                                                            int2* __restrict__ mtiles,
+                                                            int32_t* __restrict__ pass_base) {
+  __shared__ int s_cnt[1024], s_act[1024], s_til[1024], s_pas[1024];
   const int e = threadIdx.x;
   const int c = e < E ? counts[e] : 0;
   const int a = c > 0 ? 1 : 0;
   const int tl = (c + kGroupBM - 1) / kGroupBM;
+  const int np = (c + kStreamMaxMT - 1) / kStreamMaxMT;
   s_cnt[e] = c;
   s_act[e] = a;
   s_til[e] = tl;
+  s_pas[e] = np;
   for (int off = 1; off < 1024; off <<= 1) {
     __syncthreads();
     const int pc = e >= off ? s_cnt[e - off] : 0;
     const int pa = e >= off ? s_act[e - off] : 0;
     const int pt = e >= off ? s_til[e - off] : 0;
+    const int pp = e >= off ? s_pas[e - off] : 0;
     __syncthreads();
     s_cnt[e] += pc;
     s_act[e] += pa;
     s_til[e] += pt;
+    s_pas[e] += pp;
   }
   __syncthreads();
   if (e < E) {
     offsets[e] = s_cnt[e] - c;
-    if (a) active[s_act[e] - 1] = e;
+    if (a) {
+      active[s_act[e] - 1] = e;
+      pass_base[s_act[e] - 1] = s_pas[e] - np;
+    }
     const int t0 = s_til[e] - tl;
     for (int i = 0; i < tl; ++i) mtiles[t0 + i] = make_int2(e, i * kGroupBM);
   }
@@ -250,15 +259,18 @@ __global__ __launch_bounds__(1024) void scan_experts_kernel(const int32_t* __res
     offsets[E] = s_cnt[e];
     hdr->n_active = s_act[e];
     hdr->n_mtiles = s_til[e];
+    hdr->n_passes = s_pas[e];
+    pass_base[s_act[e]] = s_pas[e];
   }
 }
 
 hipError_t launch_scan(int32_t* chunk_cnt, int nchunks, int E, int32_t* counts, int32_t* offsets,
-                       RouteHeader* hdr, int32_t* active, int2* mtiles, hipStream_t s) {
+                       RouteHeader* hdr, int32_t* active, int2* mtiles, int32_t* pass_base,
+                       hipStream_t s) {
   scan_chunks_kernel<<<dim3((E + 3) / 4), 256, 0, s>>>(chunk_cnt, nchunks, E, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  scan_experts_kernel<<<1, 1024, 0, s>>>(counts, E, offsets, hdr, active, mtiles);
+  scan_experts_kernel<<<1, 1024, 0, s>>>(counts, E, offsets, hdr, active, mtiles, pass_base);
   return hipGetLastError();
 }
 

@@ -4,58 +4,438 @@
 // expert matmuls are bound by reading the expert weights from HBM once.  The
 // weights stay in their grouped layout ("nemo_automodel ... state_dict_adapter",
 // Glm4MoeStateDictAdapter: gate_and_up_projs [E, d, 2I] and down_projs [E, I, d],
-// both with the output dimension contiguous), so a lane reads 16 contiguous
-// bytes of one weight row and the wavefront reads whole row segments; the few
-// token activations are broadcast and the products are fp32 FMAs.
+// both with the output dimension contiguous).
 //
-// Work unit: (active expert, column slice).  Inside a 256-thread block, CL
-// lanes cover the slice's columns (16 bytes each) and the 256/CL row groups
-// split the contraction dimension into contiguous ranges; the row-group partial
-// sums are reduced through LDS in a fixed order, so results are bitwise
-// reproducible.  gate_up slices pair gate columns [c, c+w) with up columns
-// [I+c, I+c+w) so that silu(gate)*up is formed in the block
-// ("GLM-5 · Input features", excerpt mlp: the SwiGLU form).
+// Row streaming.  A block reads whole weight rows, one 16-byte vector per lane:
+// for down, 768 lanes cover a 12 KiB row of d = 6144 columns; for gate_up, 512
+// lanes cover the 4 KiB of gate and the 4 KiB of up columns of a row (I = 2048):
+// the first half of each wave reads gate columns and the second half the
+// matching up columns, and the halves meet through a lane shuffle to form
+// silu(gate) * up ("GLM-5 · Input features", excerpt mlp: the SwiGLU form).
+// Wider outputs take several strips of that many columns.  The few token
+// activations are the same for every lane (scalar loads) and the products are
+// fp32 FMAs kept in registers: no LDS and no reduction across lanes.
+//
+// Balance.  The launch's work is the list of items (active expert i, pass p,
+// strip s) in that order, a pass being up to kStreamMaxMT of the expert's tokens,
+// each item cut into K / kRsChunk chunks of kRsChunk weight rows.  When there are
+// no more items than resident blocks, block b takes item b whole.  Otherwise the P
+// resident blocks split the chunk list into equal contiguous ranges, lo(b) =
+// floor(b * total / P), so every block reads the same number of weight bytes and
+// the launch ends without a tail of lone blocks (the Stream-K decomposition of
+// Osama et al., 2023, applied to a memory-bound product).  An item whose chunks
+// fall in several blocks leaves one fp32 partial sum per part in a slot, and a
+// small fixup kernel launched right after adds the parts in block order and
+// applies the epilogue; the kernel boundary orders the two, so no block ever
+// waits for or signals another.
+#include <algorithm>
+#include <atomic>
+
 #include "common.h"
-#include "dev_stream.h"
 #include "kernels.h"
 
 namespace moe {
 
-template <typename T, int CL, bool GU>
-__global__ __launch_bounds__(kStreamThreads) void stream_kernel(GroupArgs g, const T* __restrict__ A,
-                                                                const T* __restrict__ Wall,
-                                                                T* __restrict__ out,
-                                                                int n_slices) {
-  extern __shared__ float red[];
-  const int u = blockIdx.x;
-  const int ai = u / n_slices, slice = u % n_slices;
-  if (ai >= g.hdr->n_active) return;
-  stream_item<T, CL, GU>(g, A, Wall, out, g.active[ai], slice, red);
+constexpr int kRsChunk = 16;  // weight rows of the smallest K range
+
+// Lanes of a block: whole rows of the GLM-5 shapes (gate_up: 4 KiB of gate and
+// 4 KiB of up columns, I = 2048; down: 12 KiB, d = 6144).
+template <bool GU>
+__host__ __device__ constexpr int rs_threads() { return GU ? 512 : 768; }
+
+// Output columns of one item (a strip): one 16-byte vector per lane for down;
+// for gate_up half the lanes read gate and half up columns.
+template <typename T, bool GU>
+__host__ __device__ constexpr int rs_strip_cols() {
+  return (GU ? rs_threads<GU>() / 2 : rs_threads<GU>()) * (16 / (int)sizeof(T));
 }
 
-template <typename T, int CL, bool GU>
-static hipError_t launch_stream(const GroupArgs& g, const void* A, const void* W, void* out,
-                                hipStream_t s) {
-  using S = StreamShape<T, CL, GU>;
-  const int width = GU ? g.I : g.d;
-  const int n_slices = (width + S::SW - 1) / S::SW;
-  const size_t lds = (size_t)S::RG * kStreamMaxMT * S::RED_COLS * sizeof(float);
-  const int64_t blocks = (int64_t)g.E * n_slices;
-  stream_kernel<T, CL, GU><<<dim3((unsigned)blocks), kStreamThreads, lds, s>>>(
-      g, (const T*)A, (const T*)W, (T*)out, n_slices);
+// Equal split of `total` chunks over `blocks` blocks.
+struct RsRange {
+  int64_t total;
+  int blocks;
+  __device__ __forceinline__ int64_t lo(int b) const { return (int64_t)b * total / blocks; }
+  // The block whose range holds chunk x: the largest b with lo(b) <= x.
+  __device__ __forceinline__ int block_of(int64_t x) const {
+    int b = (int)min<int64_t>(blocks - 1, x * blocks / total);
+    while (b + 1 < blocks && lo(b + 1) <= x) ++b;
+    while (lo(b) > x) --b;
+    return b;
+  }
+};
+
+// Geometry of one launch, the same in the main and the fixup kernel.
+template <typename T, bool GU>
+struct RsGeom {
+  int K, n_out, strips, C;
+  int64_t ldw;
+  RsRange R;
+  __device__ __forceinline__ RsGeom(const GroupArgs& g, int n_passes, int blocks) {
+    K = GU ? g.d : g.I;
+    n_out = GU ? g.I : g.d;
+    ldw = GU ? 2 * (int64_t)g.I : (int64_t)g.d;
+    strips = (n_out + rs_strip_cols<T, GU>() - 1) / rs_strip_cols<T, GU>();
+    C = K / kRsChunk;
+    const int64_t items = (int64_t)n_passes * strips;
+    R.total = items * C;
+    // With no more items than blocks each block takes one whole item (no cuts).
+    R.blocks = items <= blocks ? (int)max<int64_t>(items, 1) : blocks;
+  }
+};
+
+// Tokens and weights of an item.
+struct RsItem {
+  int e, seg, m0, mt, strip;
+};
+
+// Item `item` given the pass prefix s_pass[0..n_active] and the active expert
+// index `ai` of an earlier item (or 0): the active expert of pass pidx is the
+// last i with s_pass[i] <= pidx.
+template <bool SEARCH>
+__device__ __forceinline__ RsItem rs_item(const GroupArgs& g, const int* s_pass, int n_active,
+                                          int strips, int64_t item, int* ai) {
+  const int pidx = (int)(item / strips);
+  if (SEARCH) {
+    int l = 0, r = n_active - 1;
+    while (l < r) {
+      const int mid = (l + r + 1) / 2;
+      if (s_pass[mid] <= pidx) l = mid; else r = mid - 1;
+    }
+    *ai = l;
+  } else {
+    while (s_pass[*ai + 1] <= pidx) ++*ai;
+  }
+  RsItem it;
+  it.e = g.active[*ai];
+  it.seg = g.offsets[it.e];
+  it.m0 = (pidx - s_pass[*ai]) * kStreamMaxMT;
+  it.mt = min(kStreamMaxMT, g.counts[it.e] - it.m0);
+  it.strip = (int)(item % strips);
+  return it;
+}
+
+// Columns of this lane: output columns [ocol, ocol + V) of the strip, read from
+// weight column wcol (the up half for gate_up lanes in the second half of a
+// wave).  In a partial-sum slot row (gate sums, then up sums for gate_up) the
+// lane's V sums sit as V / 4 groups of four, group j at spos + j * sgap, so that
+// each group's store by a wave covers one contiguous kilobyte.
+template <typename T, bool GU>
+struct RsLane {
+  int grp, ocol, spos, sgap;
+  int64_t wcol;
+  bool is_up, ok;
+  __device__ __forceinline__ RsLane(const GroupArgs& g, int n_out, int strip) {
+    constexpr int V = Elem<T>::kVec, SW = rs_strip_cols<T, GU>();
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    is_up = GU && lane >= kWave / 2;
+    grp = GU ? wave * (kWave / 2) + lane % (kWave / 2) : tid;
+    ocol = strip * SW + grp * V;
+    ok = ocol < n_out;  // n_out is a multiple of V
+    wcol = (is_up ? (int64_t)g.I : 0) + ocol;
+    const int wq = min(SW, n_out);  // slot floats of the gate (or the only) half
+    spos = (is_up ? wq : 0) + grp * 4;
+    sgap = wq / V * 4;
+  }
+};
+
+// fp32 words of a slot row: the strip's columns (gate, then up for gate_up).
+template <typename T, bool GU>
+__device__ __forceinline__ int64_t rs_slot_ld(int n_out) {
+  return (GU ? 2 : 1) * (int64_t)min(rs_strip_cols<T, GU>(), n_out);
+}
+
+// RPI consecutive elements of one fp32 activation row.
+template <typename T, int RPI>
+__device__ __forceinline__ void load_act(const T* p, float* f) {
+#pragma unroll
+  for (int r = 0; r < RPI; r += 4) Elem<float>::unpack(ldg16(p + r), f + r);
+}
+
+// c + x.lo * y.lo + x.hi * y.hi for two packed bf16 pairs (v_dot2c_f32_bf16).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t x, uint32_t y, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x),
+                                         __builtin_bit_cast(bf16x2_t, y), c, false);
+}
+
+// acc[m][c] = sum over weight rows [k0, k1) of A[row m][k] * W[k][wcol + c].
+//   gate_up: A = h [T, d] (rows gathered by perm_token), W = gate_up[e] [d, 2I]
+//   down:    A = act [rows, I],                          W = down[e] [I, d]
+template <typename T, bool GU, int MT>
+__device__ __forceinline__ void rs_accumulate(const GroupArgs& g, const T* __restrict__ A,
+                                              int64_t lda, const T* __restrict__ W, int64_t ldw,
+                                              const RsItem& it, const RsLane<T, GU>& ln, int k0,
+                                              int k1, float (&acc)[MT][Elem<T>::kVec]) {
+  constexpr int V = Elem<T>::kVec;
+  constexpr int RPI = 8;  // rows per step: 8 weight vectors in flight per lane
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int c = 0; c < V; ++c) acc[m][c] = 0.f;
+  if (!ln.ok) return;
+  const T* arow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int mm = m < it.mt ? m : it.mt - 1;  // rows past mt repeat the last one, never stored
+    const int64_t prow = it.seg + it.m0 + mm;
+    const int64_t r = GU ? (int64_t)g.perm_token[prow] : prow;
+    arow[m] = A + r * lda;
+  }
+  const T* wp = W + (int64_t)k0 * ldw + ln.wcol;
+  for (int k = k0; k < k1; k += RPI, wp += (int64_t)RPI * ldw) {
+    uint4 wv[RPI];
+#pragma unroll
+    for (int r = 0; r < RPI; ++r) wv[r] = ldg16_stream(wp + (int64_t)r * ldw);
+    if constexpr (sizeof(T) == 2) {
+      // bf16: products of row pairs (k + 2p, k + 2p + 1) with v_dot2c_f32_bf16,
+      // acc += a[2p] * w[2p][c] + a[2p + 1] * w[2p + 1][c].  A row's 16 bytes
+      // hold the activation pairs in order; the weight pairs are gathered from
+      // two rows' words (cols c, c + 1 each) with byte permutes.
+      uint32_t a[MT][RPI / 2];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const uint4 q = ldg16(arow[m] + k);
+        a[m][0] = q.x; a[m][1] = q.y; a[m][2] = q.z; a[m][3] = q.w;
+      }
+#pragma unroll
+      for (int p = 0; p < RPI / 2; ++p) {
+        const uint32_t lo[4] = {wv[2 * p].x, wv[2 * p].y, wv[2 * p].z, wv[2 * p].w};
+        const uint32_t hi[4] = {wv[2 * p + 1].x, wv[2 * p + 1].y, wv[2 * p + 1].z,
+                                wv[2 * p + 1].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w0 = __builtin_amdgcn_perm(hi[q], lo[q], 0x05040100u);  // column 2q
+          const uint32_t w1 = __builtin_amdgcn_perm(hi[q], lo[q], 0x07060302u);  // column 2q + 1
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            acc[m][2 * q] = dot2_bf16(a[m][p], w0, acc[m][2 * q]);
+            acc[m][2 * q + 1] = dot2_bf16(a[m][p], w1, acc[m][2 * q + 1]);
+          }
+        }
+      }
+    } else {
+      float a[MT][RPI];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) load_act<T, RPI>(arow[m] + k, a[m]);
+#pragma unroll
+      for (int r = 0; r < RPI; ++r) {
+        float f[V];
+        Elem<T>::unpack(wv[r], f);
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int c = 0; c < V; ++c) acc[m][c] += a[m][r] * f[c];
+      }
+    }
+  }
+}
+
+// Stores an item's outputs: act = silu(gate) * up for gate_up (the up sums sit
+// in the lane kWave / 2 further on; every lane takes part in the shuffle), the
+// sums themselves for down.
+template <typename T, bool GU, int MT>
+__device__ __forceinline__ void rs_store(const float (&acc)[MT][Elem<T>::kVec], const RsItem& it,
+                                         const RsLane<T, GU>& ln, int n_out,
+                                         T* __restrict__ out) {
+  constexpr int V = Elem<T>::kVec;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m >= it.mt) break;
+    float v[V];
+    if constexpr (GU) {
+#pragma unroll
+      for (int c = 0; c < V; ++c) {
+        const float u = __shfl_xor(acc[m][c], kWave / 2, kWave);
+        v[c] = silu(acc[m][c]) * u;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < V; ++c) v[c] = acc[m][c];
+    }
+    if (ln.ok && !ln.is_up)
+      stg16(out + (int64_t)(it.seg + it.m0 + m) * n_out + ln.ocol, Elem<T>::pack(v));
+  }
+}
+
+// Slot of block b's part of an item starting at chunk item0: 0 when the part
+// starts the block's range, else 1 (the part then ends the range).
+__device__ __forceinline__ float* rs_slot(const StreamFix& fx, const RsRange& R, int b,
+                                          int64_t item0) {
+  const int sl = item0 > R.lo(b) ? 1 : 0;
+  return fx.parts + ((int64_t)b * 2 + sl) * fx.slot_floats;
+}
+
+template <typename T, bool GU, int MT>
+__device__ __forceinline__ void rs_part(const GroupArgs& g, const StreamFix& fx,
+                                        const RsGeom<T, GU>& G, const T* __restrict__ A,
+                                        const T* __restrict__ Wall, const RsItem& it, int c0,
+                                        int c1, int b, int64_t item0, T* __restrict__ out) {
+  constexpr int V = Elem<T>::kVec;
+  const RsLane<T, GU> ln(g, G.n_out, it.strip);
+  const T* W = Wall + (int64_t)it.e * G.K * G.ldw;
+  float acc[MT][V];
+  rs_accumulate<T, GU, MT>(g, A, G.K, W, G.ldw, it, ln, c0 * kRsChunk, c1 * kRsChunk, acc);
+  if (c0 == 0 && c1 == G.C) {
+    rs_store<T, GU, MT>(acc, it, ln, G.n_out, out);
+    return;
+  }
+  if (!ln.ok) return;
+  float* mine = rs_slot(fx, G.R, b, item0);
+  const int64_t ld = rs_slot_ld<T, GU>(G.n_out);
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m >= it.mt) break;
+#pragma unroll
+    for (int c = 0; c < V; c += 4)
+      *reinterpret_cast<float4*>(mine + m * ld + ln.spos + (c / 4) * ln.sgap) =
+          make_float4(acc[m][c], acc[m][c + 1], acc[m][c + 2], acc[m][c + 3]);
+  }
+}
+
+template <typename T, bool GU>
+__global__ __launch_bounds__(rs_threads<GU>()) void stream_kernel(GroupArgs g, StreamFix fx,
+                                                                  const T* __restrict__ A,
+                                                                  const T* __restrict__ Wall,
+                                                                  T* __restrict__ out) {
+  __shared__ int s_pass[kMaxStreamExperts + 1];
+  const int n_active = g.hdr->n_active;
+  for (int i = threadIdx.x; i <= n_active; i += rs_threads<GU>()) s_pass[i] = g.pass_base[i];
+  __syncthreads();
+  const RsGeom<T, GU> G(g, s_pass[n_active], fx.blocks);
+  const int b = blockIdx.x;
+  if (b >= G.R.blocks) return;
+  const int64_t lo = G.R.lo(b), hi = G.R.lo(b + 1);
+  int ai = 0;
+  for (int64_t pos = lo; pos < hi;) {
+    const int64_t item = pos / G.C;
+    const int c0 = (int)(pos - item * G.C);
+    const int c1 = (int)min<int64_t>(G.C, c0 + (hi - pos));
+    const RsItem it = pos == lo ? rs_item<true>(g, s_pass, n_active, G.strips, item, &ai)
+                                : rs_item<false>(g, s_pass, n_active, G.strips, item, &ai);
+#define MOE_PART(MT) rs_part<T, GU, MT>(g, fx, G, A, Wall, it, c0, c1, b, item * G.C, out)
+    if (it.mt == 1) MOE_PART(1);
+    else if (it.mt == 2) MOE_PART(2);
+    else if (it.mt <= 4) MOE_PART(4);
+    else MOE_PART(8);
+#undef MOE_PART
+    pos += c1 - c0;
+  }
+}
+
+// Finishes the item that runs past the end of block b's range, when the item
+// starts in that range (so each cut item is finished once): adds its parts'
+// slots in block order and stores the outputs.
+template <typename T, bool GU, int MT>
+__device__ __forceinline__ void rs_finish(const GroupArgs& g, const StreamFix& fx,
+                                          const RsGeom<T, GU>& G, const RsItem& it, int b,
+                                          int64_t item0, T* __restrict__ out) {
+  constexpr int V = Elem<T>::kVec;
+  const RsLane<T, GU> ln(g, G.n_out, it.strip);
+  const int64_t ld = rs_slot_ld<T, GU>(G.n_out);
+  const int bl = G.R.block_of(item0 + G.C - 1);
+  float acc[MT][V];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int c = 0; c < V; ++c) acc[m][c] = 0.f;
+  if (ln.ok) {
+    for (int bb = b; bb <= bl; ++bb) {
+      if (G.R.lo(bb) == G.R.lo(bb + 1)) continue;  // empty range
+      const float* src = rs_slot(fx, G.R, bb, item0);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m >= it.mt) break;
+#pragma unroll
+        for (int c = 0; c < V; c += 4) {
+          const float4 v =
+              *reinterpret_cast<const float4*>(src + m * ld + ln.spos + (c / 4) * ln.sgap);
+          acc[m][c] += v.x;
+          acc[m][c + 1] += v.y;
+          acc[m][c + 2] += v.z;
+          acc[m][c + 3] += v.w;
+        }
+      }
+    }
+  }
+  rs_store<T, GU, MT>(acc, it, ln, G.n_out, out);
+}
+
+template <typename T, bool GU>
+__global__ __launch_bounds__(rs_threads<GU>()) void stream_fixup_kernel(GroupArgs g,
+                                                                        StreamFix fx,
+                                                                        T* __restrict__ out) {
+  __shared__ int s_pass[kMaxStreamExperts + 1];
+  const int n_active = g.hdr->n_active;
+  for (int i = threadIdx.x; i <= n_active; i += rs_threads<GU>()) s_pass[i] = g.pass_base[i];
+  __syncthreads();
+  const RsGeom<T, GU> G(g, s_pass[n_active], fx.blocks);
+  const int b = blockIdx.x;
+  if (b + 1 >= G.R.blocks) return;
+  const int64_t lo = G.R.lo(b), x = G.R.lo(b + 1);
+  if (lo == x || x >= G.R.total || x % G.C == 0) return;  // empty range, or no item cut at its end
+  const int64_t item = x / G.C, item0 = item * G.C;
+  if (item0 < lo) return;  // the item started in an earlier block, which finishes it
+  int ai = 0;
+  const RsItem it = rs_item<true>(g, s_pass, n_active, G.strips, item, &ai);
+#define MOE_FIN(MT) rs_finish<T, GU, MT>(g, fx, G, it, b, item0, out)
+  if (it.mt == 1) MOE_FIN(1);
+  else if (it.mt == 2) MOE_FIN(2);
+  else if (it.mt <= 4) MOE_FIN(4);
+  else MOE_FIN(8);
+#undef MOE_FIN
+}
+
+// Blocks of stream_kernel<T, GU> resident on the current device at once (all
+// compute units), capped at kStreamMaxBlocks; queried once per device.
+template <typename T, bool GU>
+static hipError_t resident_blocks(int* blocks) {
+  static std::atomic<int> cached[64];  // zero-initialised (static storage)
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int cus = 0, per_cu = 0;
+    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stream_kernel<T, GU>,
+                                                       rs_threads<GU>(), 0);
+    if (err != hipSuccess) return err;
+    n = std::max(1, std::min(kStreamMaxBlocks, std::max(per_cu, 1) * std::max(cus, 1)));
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  *blocks = n;
+  return hipSuccess;
+}
+
+template <typename T, bool GU>
+static hipError_t launch_stream(const GroupArgs& g, const StreamFix& fx_in, const void* A,
+                                const void* W, void* out, hipStream_t s) {
+  StreamFix fx = fx_in;
+  hipError_t err = resident_blocks<T, GU>(&fx.blocks);
+  if (err != hipSuccess) return err;
+  if (fx.blocks < 1 || fx.blocks > kStreamMaxBlocks || g.E > kMaxStreamExperts)
+    return hipErrorInvalidValue;
+  stream_kernel<T, GU><<<dim3((unsigned)fx.blocks), rs_threads<GU>(), 0, s>>>(
+      g, fx, (const T*)A, (const T*)W, (T*)out);
+  err = hipGetLastError();
+  if (err != hipSuccess || fx.blocks == 1) return err;
+  stream_fixup_kernel<T, GU><<<dim3((unsigned)fx.blocks - 1), rs_threads<GU>(), 0, s>>>(
+      g, fx, (T*)out);
   return hipGetLastError();
 }
 
-hipError_t launch_stream_gate_up(int dtype, const GroupArgs& g, const void* h,
-                                 const void* gate_up, void* act, hipStream_t s) {
-  if (dtype == kBF16) return launch_stream<bf16, 32, true>(g, h, gate_up, act, s);
-  return launch_stream<float, 32, true>(g, h, gate_up, act, s);
+hipError_t launch_stream_gate_up(int dtype, const GroupArgs& g, const StreamFix& fx,
+                                 const void* h, const void* gate_up, void* act, hipStream_t s) {
+  if (dtype == kBF16) return launch_stream<bf16, true>(g, fx, h, gate_up, act, s);
+  return launch_stream<float, true>(g, fx, h, gate_up, act, s);
 }
 
-hipError_t launch_stream_down(int dtype, const GroupArgs& g, const void* act, const void* down,
-                              void* y, hipStream_t s) {
-  if (dtype == kBF16) return launch_stream<bf16, 64, false>(g, act, down, y, s);
-  return launch_stream<float, 64, false>(g, act, down, y, s);
+hipError_t launch_stream_down(int dtype, const GroupArgs& g, const StreamFix& fx,
+                              const void* act, const void* down, void* y, hipStream_t s) {
+  if (dtype == kBF16) return launch_stream<bf16, false>(g, fx, act, down, y, s);
+  return launch_stream<float, false>(g, fx, act, down, y, s);
 }
 
 }  // namespace moe

@@ -38,8 +38,23 @@ inline void mfma_nt_tile(int64_t M, int* tm, int* tn, int* tk) {
 struct RouteHeader {
   int32_t n_active;  // experts with at least one token
   int32_t n_mtiles;  // M-tiles of kGroupBM rows over all experts
-  int32_t pad[14];
+  int32_t n_passes;  // passes of the streaming kernels: sum over experts of ceil(count / kStreamMaxMT)
+  int32_t pad[13];
 };
+
+// Streaming expert kernels: tokens of one expert handled per pass over its
+// weights, most blocks of one launch, most experts.
+constexpr int kStreamMaxMT = 8;
+constexpr int kStreamMaxBlocks = 256;
+constexpr int kMaxStreamExperts = 1024;
+// fp32 words of one partial-sum slot of the streaming kernels: kStreamMaxMT rows
+// of an item's weight columns, one 16-byte vector per lane at most (gate_up: 256
+// lanes of gate and 256 of up columns; down: 768 lanes), enough for both kernels.
+inline int64_t stream_slot_floats(int dtype, int I, int d) {
+  const int64_t v = dtype == kBF16 ? 8 : 4;
+  const int64_t gu = 2 * (256 * v < I ? 256 * v : I), dn = 768 * v < d ? 768 * v : d;
+  return (int64_t)kStreamMaxMT * (gu > dn ? gu : dn);
+}
 
 // ---------------------------------------------------------------- small kernels
 // h[t] = RMSNorm(x[t]) * w for T rows of d features; rows ldx / ldh elements apart.
@@ -67,8 +82,11 @@ hipError_t launch_topk(const float* logit_part, int splits, const float* corr_bi
                        int E, int k, float routed_scale, int32_t* topk_idx, float* topk_w,
                        int32_t* chunk_cnt, hipStream_t s);
 
+// Also writes pass_base[i], the first streaming pass of the i-th active expert
+// (i <= n_active; pass_base[n_active] = n_passes).
 hipError_t launch_scan(int32_t* chunk_cnt, int nchunks, int E, int32_t* counts, int32_t* offsets,
-                       RouteHeader* hdr, int32_t* active, int2* mtiles, hipStream_t s);
+                       RouteHeader* hdr, int32_t* active, int2* mtiles, int32_t* pass_base,
+                       hipStream_t s);
 
 hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* chunk_base,
                           const int32_t* offsets, int64_t T, int E, int k, int32_t* perm_token,
@@ -104,15 +122,26 @@ struct GroupArgs {
   const int32_t* active;     // compacted active expert ids (stream kernels)
   const int2* mtiles;        // (expert, first row) per M-tile (MFMA kernels)
   const int32_t* perm_token; // token of each permuted row (gate_up gathers h rows)
+  const int32_t* pass_base;  // first streaming pass of each active expert (stream kernels)
   int E, d, I;
 };
 
+// Work balance of the streaming kernels: `blocks` blocks share the launch's rows
+// of weights equally, so an (expert, pass, column strip) item can be split
+// between blocks; each part leaves its fp32 sums in a slot of `parts` (two per
+// block) and a fixup kernel adds them up.
+struct StreamFix {
+  float* parts;         // 2 * kStreamMaxBlocks slots of slot_floats words
+  int64_t slot_floats;  // stream_slot_floats(dtype, I, d)
+  int blocks;           // set by the launcher: resident blocks, at most kStreamMaxBlocks
+};
+
 // act[row][n] = D(silu(h[tok] . G[:, n]) * (h[tok] . G[:, I + n]))  for every permuted row
-hipError_t launch_stream_gate_up(int dtype, const GroupArgs& g, const void* h,
-                                 const void* gate_up, void* act, hipStream_t s);
+hipError_t launch_stream_gate_up(int dtype, const GroupArgs& g, const StreamFix& fx,
+                                 const void* h, const void* gate_up, void* act, hipStream_t s);
 // y[row][c] = D(act[row] . down[e][:, c])
-hipError_t launch_stream_down(int dtype, const GroupArgs& g, const void* act, const void* down,
-                              void* y, hipStream_t s);
+hipError_t launch_stream_down(int dtype, const GroupArgs& g, const StreamFix& fx,
+                              const void* act, const void* down, void* y, hipStream_t s);
 
 hipError_t launch_mfma_gate_up(const GroupArgs& g, int max_mtiles, const void* h,
                                const void* gate_up, void* act, hipStream_t s);

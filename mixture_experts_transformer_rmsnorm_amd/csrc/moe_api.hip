@@ -75,7 +75,8 @@ Split nt_split(int64_t M, int64_t N, int64_t K, int tm, int tn, int tk, int max_
 
 struct Layout {
   size_t h, logits, topk_idx, topk_w, chunk_cnt, counts, offsets, hdr, active, mtiles,
-      perm_token, row_of, act, y, sh_gu, act_s, sh_dn, sync, total;
+      perm_token, row_of, pass_base, s_parts, act, y, sh_gu, act_s, sh_dn, sync,
+      total;
 };
 
 struct EventPair {
@@ -169,6 +170,12 @@ void make_layout(moe_plan* p) {
   L.mtiles = take((size_t)(cdiv(A, kGroupBM) + std::min<int64_t>(c.n_experts, A)) * sizeof(int2));
   L.perm_token = take((size_t)A * 4);
   L.row_of = take((size_t)A * 4);
+  L.pass_base = take((size_t)(c.n_experts + 1) * 4);
+  L.s_parts = c.n_experts > 0 && c.path != MOE_PATH_MFMA
+                  ? take((size_t)kStreamMaxBlocks * 2 *
+                         stream_slot_floats(c.dtype == MOE_DTYPE_BF16 ? kBF16 : kF32,
+                                            c.moe_inter, c.dim) * 4)
+                  : 0;
   L.act = take((size_t)A * c.moe_inter * es);
   L.y = take((size_t)A * c.dim * es);
   if (c.shared_inter > 0) {
@@ -334,6 +341,8 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   int2* mtiles = (int2*)(ws + L.mtiles);
   int32_t* perm_token = (int32_t*)(ws + L.perm_token);
   int32_t* row_of = (int32_t*)(ws + L.row_of);
+  int32_t* pass_base = (int32_t*)(ws + L.pass_base);
+  float* s_parts = (float*)(ws + L.s_parts);
   void* act = ws + L.act;
   void* y = ws + L.y;
   float* sh_gu = (float*)(ws + L.sh_gu);
@@ -422,16 +431,17 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
                        chunk_cnt, s);
   });
   stage(kStScan, [&] {
-    return launch_scan(chunk_cnt, nchunks, E, counts, offsets, hdr, active, mtiles, s);
+    return launch_scan(chunk_cnt, nchunks, E, counts, offsets, hdr, active, mtiles, pass_base, s);
   });
   stage(kStScatter, [&] {
     return launch_scatter(topk_idx, chunk_cnt, offsets, T, E, k, perm_token, row_of, s);
   });
-  GroupArgs g{counts, offsets, hdr, active, mtiles, perm_token, E, d, I};
+  GroupArgs g{counts, offsets, hdr, active, mtiles, perm_token, pass_base, E, d, I};
+  const StreamFix fx{s_parts, stream_slot_floats(dt, I, d), 0};
   const int max_mtiles = (int)(cdiv(A, kGroupBM) + std::min<int64_t>(E, A));
   stage(kStGateUp, [&] {
     return mfma ? launch_mfma_gate_up(g, max_mtiles, h, gate_up, act, s)
-                : launch_stream_gate_up(dt, g, h, gate_up, act, s);
+                : launch_stream_gate_up(dt, g, fx, h, gate_up, act, s);
   });
   if (has_shared) {
     stage(kStSharedGateUp,
@@ -444,7 +454,7 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   }
   stage(kStDown, [&] {
     return mfma ? launch_mfma_down(g, max_mtiles, act, down, y, s)
-                : launch_stream_down(dt, g, act, down, y, s);
+                : launch_stream_down(dt, g, fx, act, down, y, s);
   });
   if (has_shared)
     stage(kStSharedDown, [&] {
