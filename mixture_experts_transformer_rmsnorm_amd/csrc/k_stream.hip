@@ -167,7 +167,8 @@ __device__ __forceinline__ void rs_accumulate(const GroupArgs& g, const T* __res
                                               const RsItem& it, const RsLane<T, GU>& ln, int k0,
                                               int k1, float (&acc)[MT][Elem<T>::kVec]) {
   constexpr int V = Elem<T>::kVec;
-  constexpr int RPI = 8;  // rows per step: 8 weight vectors in flight per lane
+  // rows per step: 8 (gate_up) or 16 (down) weight vectors in flight per lane
+  constexpr int RPI = GU ? 8 : 16;
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -188,15 +189,17 @@ __device__ __forceinline__ void rs_accumulate(const GroupArgs& g, const T* __res
     for (int r = 0; r < RPI; ++r) wv[r] = ldg16_stream(wp + (int64_t)r * ldw);
     if constexpr (sizeof(T) == 2) {
       // bf16: products of row pairs (k + 2p, k + 2p + 1) with v_dot2c_f32_bf16,
-      // acc += a[2p] * w[2p][c] + a[2p + 1] * w[2p + 1][c].  A row's 16 bytes
-      // hold the activation pairs in order; the weight pairs are gathered from
-      // two rows' words (cols c, c + 1 each) with byte permutes.
+      // acc += a[2p] * w[2p][c] + a[2p + 1] * w[2p + 1][c].  An activation row's
+      // 16-byte pieces hold the pairs in order; the weight pairs are gathered
+      // from two rows' words (cols c, c + 1 each) with byte permutes.
       uint32_t a[MT][RPI / 2];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const uint4 q = ldg16(arow[m] + k);
-        a[m][0] = q.x; a[m][1] = q.y; a[m][2] = q.z; a[m][3] = q.w;
-      }
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int h = 0; h < RPI / 8; ++h) {
+          const uint4 q = ldg16(arow[m] + k + 8 * h);
+          a[m][4 * h] = q.x; a[m][4 * h + 1] = q.y; a[m][4 * h + 2] = q.z; a[m][4 * h + 3] = q.w;
+        }
 #pragma unroll
       for (int p = 0; p < RPI / 2; ++p) {
         const uint32_t lo[4] = {wv[2 * p].x, wv[2 * p].y, wv[2 * p].z, wv[2 * p].w};

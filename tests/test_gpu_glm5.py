@@ -106,6 +106,14 @@ def test_glm5_decode_stream(glm5_weights):
     _check(cfg, glm5_weights, path=moe.MOE_PATH_STREAM)
 
 
+def test_glm5_stream_split_items(glm5_weights):
+    """256 tokens on the streaming path: more (expert, pass) items than resident
+    blocks, so the balanced launch splits items between blocks and the fixup
+    kernel finishes them."""
+    cfg = workloads.config("glm5_decode", T=256)
+    _check(cfg, glm5_weights, path=moe.MOE_PATH_STREAM, n_sample=N_SAMPLE)
+
+
 @pytest.mark.skip(reason="the fused decode kernel is switched off: its first GPU run did not "
                          "finish and the cause has not been established")
 def test_glm5_decode_fused(glm5_weights):

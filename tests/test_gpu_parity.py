@@ -103,6 +103,19 @@ def test_out_aliases_x_and_repeatability():
     check_close(o1.float().cpu().numpy(), o2.float().cpu().numpy(), "bf16", "stream-vs-mfma")
 
 
+def test_stream_split_items_repeatable():
+    """Streaming path with more (expert, pass) items than resident blocks (items
+    split between blocks, finished by the fixup kernel): parity and bitwise
+    repeatability."""
+    cfg = workloads.config("tiny_fp32", dtype="bf16", T=520, E=32, k=6, d=256, I=320, Is=128)
+    cfg, small, route, tin = prepare(cfg, seed=11)
+    cnt = np.bincount(route["idx"].ravel(), minlength=cfg.E)
+    assert int(np.sum((cnt + 7) // 8)) > 256  # more passes than blocks
+    block, out1 = _full_check(cfg, small, route, tin, STREAM)
+    _, out2 = run_gpu(cfg, tin, STREAM, block=block)
+    assert torch.equal(out1, out2), "bitwise repeatability"
+
+
 def test_smaller_call_after_larger_reuses_workspace():
     cfg, small, route, tin = prepare(workloads.config("tiny_fp32", dtype="bf16", T=256, E=16,
                                                       k=4, d=256, I=128, Is=128))
