@@ -45,9 +45,15 @@
  *      shared_down   [d, Is]       D
  *  - Ownership: the caller allocates and owns every tensor and the workspace.
  *    The library never allocates device memory, frees, or synchronises inside
- *    moe_block_forward.  A plan holds host memory only and is immutable after
- *    creation, so one plan may serve several threads.  A workspace serves one
- *    call in flight at a time; later calls on the same stream may reuse it.
+ *    moe_block_forward.  A plan's configuration is immutable after creation and
+ *    one plan may serve several threads.  A plan also owns, per device, one
+ *    non-blocking side stream and two events (made on the first MoE call with a
+ *    shared expert on that device, released by moe_plan_destroy): the shared
+ *    expert runs there, forked from and joined back to the call's stream, so
+ *    the call stays ordered on its stream (and can be captured into a graph);
+ *    concurrent calls on one plan serialise only their host-side enqueueing.
+ *    A workspace serves one call in flight at a time; later calls on the same
+ *    stream may reuse it.
  *  - Aliasing: out may alias x (in-place residual); no other aliasing.
  *  - Errors: arguments are validated synchronously before anything is
  *    enqueued; on error nothing is written and a status is returned.  Device
@@ -251,7 +257,8 @@ MOE_API int32_t moe_plan_path(moe_plan_t plan, int64_t num_tokens, int32_t top_k
 
 /* Per-stage GPU timing.  stage_mask selects stages (bit s = stage s, see
  * moe_stage_name; 0 disables).  While set, moe_block_forward records a HIP
- * event before and after each selected stage's kernels on the call's stream;
+ * event before and after each selected stage's kernels on the stream they run
+ * on (the call's stream, or the side stream for the shared-expert stages);
  * after the caller synchronises, moe_stage_times returns the elapsed
  * milliseconds summed per stage since the last read in ms[stage] and the number
  * of timed calls in *calls.  Timing state is the only mutable part of a plan and

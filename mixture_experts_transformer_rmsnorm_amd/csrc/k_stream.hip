@@ -368,12 +368,16 @@ __global__ __launch_bounds__(rs_threads<GU>()) void stream_fixup_kernel(GroupArg
                                                                         StreamFix fx,
                                                                         T* __restrict__ out) {
   __shared__ int s_pass[kMaxStreamExperts + 1];
+  const int b = blockIdx.x;
+  {
+    // nothing to finish when every block took whole items (or this block has no successor)
+    const RsGeom<T, GU> G0(g, g.hdr->n_passes, fx.blocks);
+    if (b + 1 >= G0.R.blocks) return;
+  }
   const int n_active = g.hdr->n_active;
   for (int i = threadIdx.x; i <= n_active; i += rs_threads<GU>()) s_pass[i] = g.pass_base[i];
   __syncthreads();
   const RsGeom<T, GU> G(g, s_pass[n_active], fx.blocks);
-  const int b = blockIdx.x;
-  if (b + 1 >= G.R.blocks) return;
   const int64_t lo = G.R.lo(b), x = G.R.lo(b + 1);
   if (lo == x || x >= G.R.total || x % G.C == 0) return;  // empty range, or no item cut at its end
   const int64_t item = x / G.C, item0 = item * G.C;

@@ -86,16 +86,27 @@ struct EventPair {
 
 }  // namespace
 
+// Side stream of the shared expert on one device, with the fork and join events.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxSideDevices = 64;
+
 struct moe_plan {
   moe_config_t cfg;
   size_t es;  // bytes per element of D
   Layout lay;
-  // stage timing (the only mutable state of a plan)
+  // stage timing
   std::mutex tmu;
   int32_t timing_mask = 0;
   int64_t timed_calls = 0;
   std::vector<EventPair> pending;
   std::vector<hipEvent_t> pool;
+  // shared-expert side streams, created on first use per device; smu is held
+  // from a call's fork until its join is enqueued
+  std::mutex smu;
+  SideStream side[kMaxSideDevices];
 };
 
 namespace {
@@ -202,6 +213,27 @@ hipEvent_t get_event(moe_plan* p) {
   return e;
 }
 
+// The side stream of the current device (created on first use: non-blocking, at
+// the default priority), or nullptr when it cannot be made; call with smu held.
+SideStream* side_stream(moe_plan* p) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return nullptr;
+  SideStream& sd = p->side[dev];
+  if (!sd.stream) {
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+      if (f) (void)hipEventDestroy(f);
+      (void)hipStreamDestroy(st);
+      return nullptr;
+    }
+    sd.stream = st, sd.fork = f, sd.join = j;
+  }
+  return &sd;
+}
+
 }  // namespace
 
 extern "C" {
@@ -265,6 +297,11 @@ moe_status_t moe_plan_destroy(moe_plan_t p) {
     (void)hipEventDestroy(ev.b);
   }
   for (auto e : p->pool) (void)hipEventDestroy(e);
+  for (auto& sd : p->side) {
+    if (sd.fork) (void)hipEventDestroy(sd.fork);
+    if (sd.join) (void)hipEventDestroy(sd.join);
+    if (sd.stream) (void)hipStreamDestroy(sd.stream);
+  }
   delete p;
   return MOE_SUCCESS;
 }
@@ -368,6 +405,7 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
     ++p->timed_calls;
   }
   hipError_t err = hipSuccess;
+  hipStream_t cs = s;  // stream the stages below are enqueued on
   auto stage = [&](int st, auto&& fn) {
     if (err != hipSuccess) return;
     EventPair ev{st, nullptr, nullptr};
@@ -379,12 +417,12 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
         err = hipErrorOutOfMemory;
         return;
       }
-      err = hipEventRecord(ev.a, s);
+      err = hipEventRecord(ev.a, cs);
       if (err != hipSuccess) return;
     }
     err = fn();
     if (timing) {
-      const hipError_t e2 = hipEventRecord(ev.b, s);
+      const hipError_t e2 = hipEventRecord(ev.b, cs);
       if (err == hipSuccess) err = e2;
       p->pending.push_back(ev);
     }
@@ -393,7 +431,7 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
                 int n_split, float* outp, int64_t N, int64_t K, int max_splits) {
     const Split sp = nt_split(T, N, K, tm, tn, tk, max_splits);
     NtArgs a{Aop, lda, B1, B2, ldb, n_split, outp, (int)T, (int)N, (int)K, sp.splits, sp.kt_per};
-    return dt == kBF16 ? launch_mfma_nt(a, s) : launch_fma_nt(dt, a, s);
+    return dt == kBF16 ? launch_mfma_nt(a, cs) : launch_fma_nt(dt, a, cs);
   };
   const Split rsplit = nt_split(T, E, d, tm, tn, tk, kMaxRouterSplits);
   const Split sdsplit =
@@ -426,6 +464,34 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   stage(kStNorm, [&] { return launch_rmsnorm(dt, x, d, norm_w, h, d, T, d, c.eps, s); });
   stage(kStRouter,
         [&] { return nt(h, d, router_w, router_w, d, E, logits, E, d, kMaxRouterSplits); });
+  // The shared expert depends only on h: it runs on a side stream, forked here and
+  // joined before the combine, beside the routing steps and the routed experts.
+  std::unique_lock<std::mutex> slock(p->smu, std::defer_lock);
+  SideStream* side = nullptr;
+  auto shared_branch = [&] {
+    stage(kStSharedGateUp, [&] {
+      return nt(h, d, shared_gate, shared_up, d, Is, sh_gu, 2 * (int64_t)Is, d, kMaxSharedSplits);
+    });
+    stage(kStSharedAct,
+          [&] { return launch_swiglu_finalize(dt, sh_gu, sgsplit.splits, T, Is, act_s, cs); });
+    stage(kStSharedDown, [&] {
+      return nt(act_s, Is, shared_down, shared_down, Is, d, sh_dn, d, Is, kMaxSharedSplits);
+    });
+  };
+  if (has_shared && err == hipSuccess) {
+    slock.lock();
+    side = side_stream(p);
+    if (side) {
+      err = hipEventRecord(side->fork, s);
+      if (err == hipSuccess) err = hipStreamWaitEvent(side->stream, side->fork, 0);
+      cs = side->stream;
+      shared_branch();
+      if (err == hipSuccess) err = hipEventRecord(side->join, side->stream);
+      cs = s;
+    } else {
+      slock.unlock();
+    }
+  }
   stage(kStTopk, [&] {
     return launch_topk(logits, rsplit.splits, corr_bias, T, E, k, routed_scale, topk_idx, topk_w,
                        chunk_cnt, s);
@@ -443,23 +509,17 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
     return mfma ? launch_mfma_gate_up(g, max_mtiles, h, gate_up, act, s)
                 : launch_stream_gate_up(dt, g, fx, h, gate_up, act, s);
   });
-  if (has_shared) {
-    stage(kStSharedGateUp,
-          [&] {
-            return nt(h, d, shared_gate, shared_up, d, Is, sh_gu, 2 * (int64_t)Is, d,
-                      kMaxSharedSplits);
-          });
-    stage(kStSharedAct,
-          [&] { return launch_swiglu_finalize(dt, sh_gu, sgsplit.splits, T, Is, act_s, s); });
-  }
   stage(kStDown, [&] {
     return mfma ? launch_mfma_down(g, max_mtiles, act, down, y, s)
                 : launch_stream_down(dt, g, fx, act, down, y, s);
   });
-  if (has_shared)
-    stage(kStSharedDown, [&] {
-      return nt(act_s, Is, shared_down, shared_down, Is, d, sh_dn, d, Is, kMaxSharedSplits);
-    });
+  if (side) {
+    const hipError_t e2 = hipStreamWaitEvent(s, side->join, 0);
+    if (err == hipSuccess) err = e2;
+    slock.unlock();
+  } else if (has_shared) {
+    shared_branch();  // no side stream: the shared expert runs in order on s
+  }
   stage(kStCombine, [&] {
     return launch_combine(dt, x, sh_dn, has_shared ? sdsplit.splits : 0, y, topk_w, row_of, T, d,
                           k, out, s);
