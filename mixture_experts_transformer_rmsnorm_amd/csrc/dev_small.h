@@ -84,6 +84,70 @@ __device__ __forceinline__ void rms_block_row(const T* xr, const T* __restrict__
   rms_row<T, 4>(xr, w, hr, d / V, threadIdx.x, 256, d, eps, reduce);
 }
 
+// Selection for one token by one wavefront from its fp32 logits l[q] (expert
+// lane + 64 q): score = sigmoid(logit); key = score + corr_bias decides; k
+// rounds of a wave-wide arg-max over (key desc, expert asc); the weights are the
+// selected unbiased scores renormalised to sum rs.  Lane j < k writes choice j of
+// token t; lane 0 counts each choice in hist (LDS) when hist is not null.
+template <int Q>
+__device__ __forceinline__ void topk_select(const float (&l)[Q], const float* __restrict__ bias,
+                                            int64_t t, int E, int k, float rs,
+                                            int32_t* __restrict__ idx_out,
+                                            float* __restrict__ w_out, int* hist) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float key[Q], sc[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int e = lane + kWave * q;
+    key[q] = -INFINITY;
+    sc[q] = 0.f;
+    if (e < E) {
+      const float sg = 1.0f / (1.0f + expf(-l[q]));
+      sc[q] = sg;
+      key[q] = sg + bias[e];
+    }
+  }
+  uint32_t taken = 0;
+  float ssum = 0.f, my_s = 0.f;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY, bs = 0.f;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int e = lane + kWave * q;
+      const bool ok = e < E && !((taken >> q) & 1u);
+      if (ok && (key[q] > bv || (key[q] == bv && e < be))) {
+        bv = key[q];
+        be = e;
+        bs = sc[q];
+      }
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, kWave);
+      const int oe = __shfl_xor(be, off, kWave);
+      const float os = __shfl_xor(bs, off, kWave);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+        bs = os;
+      }
+    }
+    if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
+    ssum += bs;
+    if (lane == j) {
+      my_s = bs;
+      my_e = be;
+    }
+    if (hist && lane == 0) atomicAdd(&hist[be], 1);
+  }
+  if (lane < k) {
+    idx_out[t * k + lane] = my_e;
+    w_out[t * k + lane] = rs * my_s / ssum;
+  }
+}
+
 template <int Q, int WAVES>
 __device__ __forceinline__ void topk_chunk(const float* __restrict__ part, int splits,
                                            const float* __restrict__ bias, int64_t T, int E, int k,
@@ -97,7 +161,6 @@ __device__ __forceinline__ void topk_chunk(const float* __restrict__ part, int s
   for (int tl = wid; tl < kChunkTokens; tl += WAVES) {
     const int64_t t = tbase + tl;
     if (t >= T) break;
-    float key[Q], sc[Q];
     float l[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) l[q] = 0.f;
@@ -120,56 +183,7 @@ __device__ __forceinline__ void topk_chunk(const float* __restrict__ part, int s
 #pragma unroll
       for (int q = 0; q < Q; ++q)
         if (lane + kWave * q < E) l[q] += pt[z * zstride + kWave * q];
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int e = lane + kWave * q;
-      key[q] = -INFINITY;
-      sc[q] = 0.f;
-      if (e < E) {
-        const float sg = 1.0f / (1.0f + expf(-l[q]));
-        sc[q] = sg;
-        key[q] = sg + bias[e];
-      }
-    }
-    uint32_t taken = 0;
-    float ssum = 0.f, my_s = 0.f;
-    int my_e = 0;
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY, bs = 0.f;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        const int e = lane + kWave * q;
-        const bool ok = e < E && !((taken >> q) & 1u);
-        if (ok && (key[q] > bv || (key[q] == bv && e < be))) {
-          bv = key[q];
-          be = e;
-          bs = sc[q];
-        }
-      }
-#pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, kWave);
-        const int oe = __shfl_xor(be, off, kWave);
-        const float os = __shfl_xor(bs, off, kWave);
-        if (ov > bv || (ov == bv && oe < be)) {
-          bv = ov;
-          be = oe;
-          bs = os;
-        }
-      }
-      if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
-      ssum += bs;
-      if (lane == j) {
-        my_s = bs;
-        my_e = be;
-      }
-      if (lane == 0) atomicAdd(&hist[be], 1);
-    }
-    if (lane < k) {
-      idx_out[t * k + lane] = my_e;
-      w_out[t * k + lane] = rs * my_s / ssum;
-    }
+    topk_select<Q>(l, bias, t, E, k, rs, idx_out, w_out, hist);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += WAVES * 64) chunk_cnt[chunk * E + e] = hist[e];

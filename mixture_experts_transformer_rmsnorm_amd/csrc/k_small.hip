@@ -189,6 +189,152 @@ hipError_t launch_topk(const float* logit_part, int splits, const float* corr_bi
   return hipGetLastError();
 }
 
+// Router selection for small batches: one block of 256 threads per token.  The
+// four wavefronts add the split-K partial logits of the splits z = w, w + 4, ...;
+// wave 0 adds the four sums in order and selects (topk_select).
+template <int Q>
+__global__ __launch_bounds__(256) void topk_small_kernel(const float* __restrict__ part, int splits,
+                                                         const float* __restrict__ bias, int64_t T,
+                                                         int E, int k, float rs,
+                                                         int32_t* __restrict__ idx_out,
+                                                         float* __restrict__ w_out) {
+  __shared__ float red[4][kWave * Q];
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int64_t t = blockIdx.x;
+  const int64_t zstride = T * (int64_t)E;
+  const float* pt = part + t * E + lane;
+  float l[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) l[q] = 0.f;
+  for (int z0 = w; z0 < splits; z0 += 16) {
+    float v[4][Q];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int z = z0 + 4 * u;
+        v[u][q] = (z < splits && lane + kWave * q < E) ? pt[z * zstride + kWave * q] : 0.f;
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < Q; ++q) l[q] += v[u][q];
+  }
+#pragma unroll
+  for (int q = 0; q < Q; ++q) red[w][lane + kWave * q] = l[q];
+  __syncthreads();
+  if (w != 0) return;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int e = lane + kWave * q;
+    l[q] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+  }
+  topk_select<Q>(l, bias, t, E, k, rs, idx_out, w_out, nullptr);
+}
+
+hipError_t launch_topk_small(const float* logit_part, int splits, const float* corr_bias,
+                             int64_t T, int E, int k, float routed_scale, int32_t* topk_idx,
+                             float* topk_w, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int q = (E + kWave - 1) / kWave;
+#define MOE_TOPKS(QQ)                                                                       \
+  topk_small_kernel<QQ><<<dim3((unsigned)T), 256, 0, s>>>(logit_part, splits, corr_bias, T, E, \
+                                                          k, routed_scale, topk_idx, topk_w)
+  if (q <= 1) MOE_TOPKS(1);
+  else if (q <= 2) MOE_TOPKS(2);
+  else if (q <= 4) MOE_TOPKS(4);
+  else if (q <= 8) MOE_TOPKS(8);
+  else MOE_TOPKS(16);
+#undef MOE_TOPKS
+  return hipGetLastError();
+}
+
+// Permutation for small batches (T * k <= kRouteSmallMax assignments, one block
+// of 1024 threads): per-expert counts (LDS atomics), then what scan_experts_kernel
+// writes (offsets, active list, M-tiles, pass prefix, header), then each
+// assignment's row: its expert's offset plus the number of earlier assignments,
+// in (token, j) order, of the same expert.  The same stable order as the chunked
+// scatter.
+__global__ __launch_bounds__(1024) void route_small_kernel(
+    const int32_t* __restrict__ topk_idx, int A, int E, int k, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, RouteHeader* __restrict__ hdr, int32_t* __restrict__ active,
+    int2* __restrict__ mtiles, int32_t* __restrict__ pass_base, int32_t* __restrict__ perm_token,
+    int32_t* __restrict__ row_of) {
+  __shared__ __attribute__((aligned(16))) int s_idx[kRouteSmallMax];
+  __shared__ int s_cnt[1024], s_act[1024], s_til[1024], s_pas[1024], s_off[1024];
+  const int e = threadIdx.x;
+  for (int i = e; i < A; i += 1024) s_idx[i] = topk_idx[i];
+  for (int i = A + e; i < ((A + 3) & ~3); i += 1024) s_idx[i] = -1;  // pad to a multiple of 4
+  s_cnt[e] = 0;
+  __syncthreads();
+  for (int i = e; i < A; i += 1024) atomicAdd(&s_cnt[s_idx[i]], 1);
+  __syncthreads();
+  const int c = e < E ? s_cnt[e] : 0;
+  const int a = c > 0 ? 1 : 0;
+  const int tl = (c + kGroupBM - 1) / kGroupBM;
+  const int np = (c + kStreamMaxMT - 1) / kStreamMaxMT;
+  s_act[e] = a;
+  s_til[e] = tl;
+  s_pas[e] = np;
+  for (int off = 1; off < 1024; off <<= 1) {
+    __syncthreads();
+    const int pc = e >= off ? s_cnt[e - off] : 0;
+    const int pa = e >= off ? s_act[e - off] : 0;
+    const int pt = e >= off ? s_til[e - off] : 0;
+    const int pp = e >= off ? s_pas[e - off] : 0;
+    __syncthreads();
+    s_cnt[e] += pc;
+    s_act[e] += pa;
+    s_til[e] += pt;
+    s_pas[e] += pp;
+  }
+  __syncthreads();
+  s_off[e] = s_cnt[e] - c;
+  if (e < E) {
+    counts[e] = c;
+    offsets[e] = s_cnt[e] - c;
+    if (a) {
+      active[s_act[e] - 1] = e;
+      pass_base[s_act[e] - 1] = s_pas[e] - np;
+    }
+    const int t0 = s_til[e] - tl;
+    for (int i = 0; i < tl; ++i) mtiles[t0 + i] = make_int2(e, i * kGroupBM);
+  }
+  if (e == E - 1) {
+    offsets[E] = s_cnt[e];
+    hdr->n_active = s_act[e];
+    hdr->n_mtiles = s_til[e];
+    hdr->n_passes = s_pas[e];
+    pass_base[s_act[e]] = s_pas[e];
+  }
+  __syncthreads();
+  for (int i = e; i < A; i += 1024) {
+    const int x = s_idx[i];
+    int rank = 0;
+    const int4* p4 = reinterpret_cast<const int4*>(s_idx);
+    const int full = i / 4;
+    for (int j = 0; j < full; ++j) {
+      const int4 v = p4[j];
+      rank += (v.x == x) + (v.y == x) + (v.z == x) + (v.w == x);
+    }
+    for (int j = full * 4; j < i; ++j) rank += s_idx[j] == x;
+    const int row = s_off[x] + rank;
+    perm_token[row] = i / k;
+    row_of[i] = row;
+  }
+}
+
+hipError_t launch_route_small(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* counts,
+                              int32_t* offsets, RouteHeader* hdr, int32_t* active, int2* mtiles,
+                              int32_t* pass_base, int32_t* perm_token, int32_t* row_of,
+                              hipStream_t s) {
+  const int64_t A = T * k;
+  if (A > kRouteSmallMax || E > 1024) return hipErrorInvalidValue;
+  route_small_kernel<<<1, 1024, 0, s>>>(topk_idx, (int)A, E, k, counts, offsets, hdr, active,
+                                        mtiles, pass_base, perm_token, row_of);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Permutation, step 1: per expert, exclusive prefix of the chunk histograms over
 // chunks (in place) and the expert's total.  One wavefront per expert.

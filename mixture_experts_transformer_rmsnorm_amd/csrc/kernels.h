@@ -88,6 +88,18 @@ hipError_t launch_scan(int32_t* chunk_cnt, int nchunks, int E, int32_t* counts, 
                        RouteHeader* hdr, int32_t* active, int2* mtiles, int32_t* pass_base,
                        hipStream_t s);
 
+// Small batches (T * k <= kRouteSmallMax, E <= 1024): selection with one block
+// per token (no chunk histograms), then the whole permutation (counts, what
+// launch_scan writes, perm_token and row_of) in one block.
+constexpr int kRouteSmallMax = 2048;
+hipError_t launch_topk_small(const float* logit_part, int splits, const float* corr_bias,
+                             int64_t T, int E, int k, float routed_scale, int32_t* topk_idx,
+                             float* topk_w, hipStream_t s);
+hipError_t launch_route_small(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* counts,
+                              int32_t* offsets, RouteHeader* hdr, int32_t* active, int2* mtiles,
+                              int32_t* pass_base, int32_t* perm_token, int32_t* row_of,
+                              hipStream_t s);
+
 hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* chunk_base,
                           const int32_t* offsets, int64_t T, int E, int k, int32_t* perm_token,
                           int32_t* row_of, hipStream_t s);

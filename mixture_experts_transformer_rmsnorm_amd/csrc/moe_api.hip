@@ -462,10 +462,9 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
     return err == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
   }
   stage(kStNorm, [&] { return launch_rmsnorm(dt, x, d, norm_w, h, d, T, d, c.eps, s); });
-  stage(kStRouter,
-        [&] { return nt(h, d, router_w, router_w, d, E, logits, E, d, kMaxRouterSplits); });
   // The shared expert depends only on h: it runs on a side stream, forked here and
-  // joined before the combine, beside the routing steps and the routed experts.
+  // joined before the combine, beside the router, the routing steps and the routed
+  // experts.
   std::unique_lock<std::mutex> slock(p->smu, std::defer_lock);
   SideStream* side = nullptr;
   auto shared_branch = [&] {
@@ -492,16 +491,27 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
       slock.unlock();
     }
   }
+  stage(kStRouter,
+        [&] { return nt(h, d, router_w, router_w, d, E, logits, E, d, kMaxRouterSplits); });
+  // Small batches: per-token selection blocks, then the whole permutation in one
+  // block; otherwise chunked selection with histograms, scans and the scatter.
+  const bool small_route = T * k <= kRouteSmallMax && E <= 1024;
   stage(kStTopk, [&] {
-    return launch_topk(logits, rsplit.splits, corr_bias, T, E, k, routed_scale, topk_idx, topk_w,
-                       chunk_cnt, s);
+    return small_route ? launch_topk_small(logits, rsplit.splits, corr_bias, T, E, k,
+                                           routed_scale, topk_idx, topk_w, s)
+                       : launch_topk(logits, rsplit.splits, corr_bias, T, E, k, routed_scale,
+                                     topk_idx, topk_w, chunk_cnt, s);
   });
   stage(kStScan, [&] {
-    return launch_scan(chunk_cnt, nchunks, E, counts, offsets, hdr, active, mtiles, pass_base, s);
+    return small_route ? launch_route_small(topk_idx, T, E, k, counts, offsets, hdr, active,
+                                            mtiles, pass_base, perm_token, row_of, s)
+                       : launch_scan(chunk_cnt, nchunks, E, counts, offsets, hdr, active, mtiles,
+                                     pass_base, s);
   });
-  stage(kStScatter, [&] {
-    return launch_scatter(topk_idx, chunk_cnt, offsets, T, E, k, perm_token, row_of, s);
-  });
+  if (!small_route)
+    stage(kStScatter, [&] {
+      return launch_scatter(topk_idx, chunk_cnt, offsets, T, E, k, perm_token, row_of, s);
+    });
   GroupArgs g{counts, offsets, hdr, active, mtiles, perm_token, pass_base, E, d, I};
   const StreamFix fx{s_parts, stream_slot_floats(dt, I, d), 0};
   const int max_mtiles = (int)(cdiv(A, kGroupBM) + std::min<int64_t>(E, A));
