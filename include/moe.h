@@ -47,11 +47,12 @@
  *    The library never allocates device memory, frees, or synchronises inside
  *    moe_block_forward.  A plan's configuration is immutable after creation and
  *    one plan may serve several threads.  A plan also owns, per device, one
- *    non-blocking side stream and two events (made on the first MoE call with a
- *    shared expert on that device, released by moe_plan_destroy): the shared
- *    expert runs there, forked from and joined back to the call's stream, so
- *    the call stays ordered on its stream (and can be captured into a graph);
- *    concurrent calls on one plan serialise only their host-side enqueueing.
+ *    non-blocking side stream and two events (made on the first call on that
+ *    device that takes the STREAM path with a shared expert, released by
+ *    moe_plan_destroy): on that path the shared expert runs there, forked from
+ *    and joined back to the call's stream, so the call stays ordered on its
+ *    stream (and can be captured into a graph); concurrent calls on one plan
+ *    serialise only their host-side enqueueing.
  *    A workspace serves one call in flight at a time; later calls on the same
  *    stream may reuse it.
  *  - Aliasing: out may alias x (in-place residual); no other aliasing.

@@ -462,9 +462,11 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
     return err == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
   }
   stage(kStNorm, [&] { return launch_rmsnorm(dt, x, d, norm_w, h, d, T, d, c.eps, s); });
-  // The shared expert depends only on h: it runs on a side stream, forked here and
+  // The shared expert depends only on h.  With the streaming expert kernels (small
+  // batches, latency-bound routing steps) it runs on a side stream, forked here and
   // joined before the combine, beside the router, the routing steps and the routed
-  // experts.
+  // experts; with the MFMA kernels its GEMMs would hold the compute units the
+  // routing steps wait for, so it runs in order after the routed experts.
   std::unique_lock<std::mutex> slock(p->smu, std::defer_lock);
   SideStream* side = nullptr;
   auto shared_branch = [&] {
@@ -477,7 +479,7 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
       return nt(act_s, Is, shared_down, shared_down, Is, d, sh_dn, d, Is, kMaxSharedSplits);
     });
   };
-  if (has_shared && err == hipSuccess) {
+  if (has_shared && !mfma && err == hipSuccess) {
     slock.lock();
     side = side_stream(p);
     if (side) {
@@ -528,7 +530,7 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
     if (err == hipSuccess) err = e2;
     slock.unlock();
   } else if (has_shared) {
-    shared_branch();  // no side stream: the shared expert runs in order on s
+    shared_branch();  // the shared expert runs in order on s
   }
   stage(kStCombine, [&] {
     return launch_combine(dt, x, sh_dn, has_shared ? sdsplit.splits : 0, y, topk_w, row_of, T, d,
