@@ -361,24 +361,25 @@ __global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p)
   const int rows = min(GB_M, p.counts[e] - m0);
   const int nkt = p.K / GB_K;
 
-  // ---- load side.  A instruction i (0..3) of wave w fills rows 8*(4w+i) ..
-  // +7 (lane/8 picks the row, lane%8 the chunk position); it is issued only if
-  // its first row lies inside the tile (rows past the end inside a partly
-  // valid group repeat the tile's last row).  B instruction i fills k-rows
-  // 2*(4w+i) + lane/32, chunk position lane%32; columns past N read column 0.
-  // Every load is in bounds, and what the clamped ones bring only reaches
-  // outputs that are never stored.
+  // ---- load side.  A instruction i (0..3) of wave w fills the 8-row group
+  // g = w + 8i, rows 8g .. 8g+7 (lane/8 picks the row, lane%8 the chunk
+  // position), so a tile with few rows spreads its A loads over all waves; it is
+  // issued only if its first row lies inside the tile (rows past the end inside
+  // a partly valid group repeat the tile's last row).  B instruction i fills
+  // k-rows 2*(4w+i) + lane/32, chunk position lane%32; columns past N read
+  // column 0.  Every load is in bounds, and what the clamped ones bring only
+  // reaches outputs that are never stored.
   const uint16_t* a_src[GB_A_LOADS];
   const uint16_t* b_src[GB_B_LOADS];
   int a_groups = 0;  // A instructions of this wave that are issued (a prefix of i)
 #pragma unroll
   for (int i = 0; i < GB_A_LOADS; ++i) {
-    const int r = 8 * (4 * w + i) + (lane >> 3);
+    const int r = 8 * (w + 8 * i) + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int64_t prow = seg + m0 + min(r, rows - 1);
     const int64_t arow = p.a_gather ? (int64_t)p.a_gather[prow] : prow;
     a_src[i] = p.A + arow * p.lda + c * 8;
-    a_groups += 8 * (4 * w + i) < rows ? 1 : 0;
+    a_groups += 8 * (w + 8 * i) < rows ? 1 : 0;
   }
   a_groups = __builtin_amdgcn_readfirstlane(a_groups);
 #pragma unroll
@@ -401,7 +402,7 @@ __global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p)
     for (int i = 0; i < GB_A_LOADS; ++i)
       if (i < a_groups)
         __builtin_amdgcn_global_load_lds(a_src[i] + kt * GB_K,
-                                         (lds_void_t*)(dst + (4 * w + i) * 512), 16, 0, 0);
+                                         (lds_void_t*)(dst + (w + 8 * i) * 512), 16, 0, 0);
   };
   auto issue_b = [&](uint16_t* dst, int kt) __attribute__((always_inline)) {
 #pragma unroll
