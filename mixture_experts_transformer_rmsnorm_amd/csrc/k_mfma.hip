@@ -414,14 +414,13 @@ __global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p)
   // ---- compute side
   const int wm = w >> 2, wn = w & 3;
   auto bcol = [&](int f) { return EPI == kEpiSwiGLU ? f * GB_ACT_COLS + wn * 32 : wn * 64 + f * 32; };
-  bool sub_ok[4];
+  // Sub-tiles j of this wave (rows 32 (wm + 2j) ..) that hold rows of the tile:
+  // a prefix j < nj, the same for the whole block, so each wave runs the K loop
+  // specialised for its nj with no branches among its MFMAs.
+  int nj = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) sub_ok[j] = 32 * (wm + 2 * j) < rows;
-  f32x16_t acc[4][2];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int f = 0; f < 2; ++f) acc[j][f] = f32x16_t{};
+  for (int j = 0; j < 4; ++j) nj += 32 * (wm + 2 * j) < rows ? 1 : 0;
+  nj = __builtin_amdgcn_readfirstlane(nj);
 
   // per-lane LDS element offsets inside a slot (the same for every step)
   const int arow_l = wm * 32 + (lane & 31);  // row inside sub-tile 0 of this wave
@@ -442,76 +441,115 @@ __global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p)
       }
   }
 
-  auto compute = [&](const uint16_t* as, const uint16_t* bs) __attribute__((always_inline)) {
+  f32x16_t acc[4][2];
 #pragma unroll
-    for (int ks = 0; ks < GB_K / 16; ++ks) {
-      bf16x8_t bf[2];
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const uint16_t* bp = bs + b_off[f][ks];
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)bp);
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(bp + 4 * GB_N));
-        typedef short s16x8_t __attribute__((ext_vector_type(8)));
-        const s16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        bf[f] = __builtin_bit_cast(bf16x8_t, v);
+    for (int f = 0; f < 2; ++f) acc[j][f] = f32x16_t{};
+
+  // The K loop for a wave with NJ sub-tiles.  The fragments of k-substep ks+1
+  // are read while the MFMAs of ks run.  Step t: wait until only this wave's B
+  // loads of step t+1 are outstanding (A of step t, issued before them, and B of
+  // step t, issued earlier, have landed), barrier (every wave's data of step t
+  // has landed and every wave is done with the slots of step t-1), refill those
+  // slots with A of step t+1 and B of step t+2, multiply step t.  Steps past the
+  // end are requested too (as copies of the last one) so that the count of
+  // loads in flight is the same at every step; they land in slots that are
+  // never read again.  Every wave passes the same barriers whatever its NJ.
+  auto k_loop = [&](auto nj_c) __attribute__((always_inline)) {
+    constexpr int NJ = decltype(nj_c)::value;
+    auto compute = [&](const uint16_t* as, const uint16_t* bs) __attribute__((always_inline)) {
+      bf16x8_t af[2][NJ > 0 ? NJ : 1], bf[2][2];
+      auto load = [&](int ks, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const uint16_t* bp = bs + b_off[f][ks];
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)bp);
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(bp + 4 * GB_N));
+          typedef short s16x8_t __attribute__((ext_vector_type(8)));
+          const s16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          bf[buf][f] = __builtin_bit_cast(bf16x8_t, v);
+        }
+        const int a_chunk = ((2 * ks + (lane >> 5)) ^ a_sw) * 8;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          af[buf][j] = *reinterpret_cast<const bf16x8_t*>(as + a_base + j * 64 * GB_K + a_chunk);
+      };
+      load(0, 0);
+#pragma unroll
+      for (int ks = 0; ks < GB_K / 16; ++ks) {
+        if (ks + 1 < GB_K / 16) load(ks + 1, (ks + 1) & 1);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+            acc[j][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][j], bf[ks & 1][f],
+                                                                acc[j][f], 0, 0, 0);
       }
-      const int a_chunk = ((2 * ks + (lane >> 5)) ^ a_sw) * 8;
+    };
+    auto step = [&](const uint16_t* a_cur, uint16_t* a_next, const uint16_t* b_cur,
+                    uint16_t* b_next, int t) __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(GB_B_LOADS));
+      __asm__ volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      issue_a(a_next, min(t + 1, nkt - 1));
+      issue_b(b_next, min(t + 2, nkt - 1));
+      if constexpr (NJ > 0) {
+        compute(a_cur, b_cur);
+        // Order: the fragments of substep 0, then each substep's MFMAs with the
+        // next substep's fragment reads (4 transposing B reads, NJ A reads)
+        // between them, so that LDS latency hides under the MFMAs.
+        constexpr int R = 4 + NJ, M = 2 * NJ;
+        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (!sub_ok[j]) continue;
-        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(as + a_base + j * 64 * GB_K + a_chunk);
+        for (int ks = 0; ks < GB_K / 16 - 1; ++ks) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
-          acc[j][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[f], acc[j][f], 0, 0, 0);
+          for (int q = 0; q < (M < R ? M : R); ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          if constexpr (R > M) __builtin_amdgcn_sched_group_barrier(0x100, R - M, 0);
+          if constexpr (M > R) __builtin_amdgcn_sched_group_barrier(0x008, M - R, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
       }
+    };
+    issue_b(sb0, 0);
+    issue_a(sa0, 0);
+    issue_b(sb1, min(1, nkt - 1));
+    int t = 0;
+    for (; t + 6 <= nkt; t += 6) {
+      step(sa0, sa1, sb0, sb2, t);
+      step(sa1, sa0, sb1, sb0, t + 1);
+      step(sa0, sa1, sb2, sb1, t + 2);
+      step(sa1, sa0, sb0, sb2, t + 3);
+      step(sa0, sa1, sb1, sb0, t + 4);
+      step(sa1, sa0, sb2, sb1, t + 5);
     }
+    if (t < nkt) step(sa0, sa1, sb0, sb2, t);
+    if (t + 1 < nkt) step(sa1, sa0, sb1, sb0, t + 1);
+    if (t + 2 < nkt) step(sa0, sa1, sb2, sb1, t + 2);
+    if (t + 3 < nkt) step(sa1, sa0, sb0, sb2, t + 3);
+    if (t + 4 < nkt) step(sa0, sa1, sb1, sb0, t + 4);
+    // no load may still be writing LDS when the block ends
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
   };
-
-  // Step t: wait until only this wave's B loads of step t+1 are outstanding
-  // (A of step t, issued before them, and B of step t, issued earlier, have
-  // landed), barrier (every wave's data of step t has landed and every wave is
-  // done with the slots of step t-1), refill those slots with A of step t+1 and
-  // B of step t+2, multiply step t.  Steps past the end are requested too (as
-  // copies of the last one) so that the count of loads in flight is the same
-  // at every step; they land in slots that are never read again.
-  auto step = [&](const uint16_t* a_cur, uint16_t* a_next, const uint16_t* b_cur, uint16_t* b_next,
-                  int t) __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(GB_B_LOADS));
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    issue_a(a_next, min(t + 1, nkt - 1));
-    issue_b(b_next, min(t + 2, nkt - 1));
-    compute(a_cur, b_cur);
-  };
-
-  issue_b(sb0, 0);
-  issue_a(sa0, 0);
-  issue_b(sb1, min(1, nkt - 1));
-  int t = 0;
-  for (; t + 6 <= nkt; t += 6) {
-    step(sa0, sa1, sb0, sb2, t);
-    step(sa1, sa0, sb1, sb0, t + 1);
-    step(sa0, sa1, sb2, sb1, t + 2);
-    step(sa1, sa0, sb0, sb2, t + 3);
-    step(sa0, sa1, sb1, sb0, t + 4);
-    step(sa1, sa0, sb2, sb1, t + 5);
+  switch (nj) {
+    case 0: k_loop(std::integral_constant<int, 0>{}); break;
+    case 1: k_loop(std::integral_constant<int, 1>{}); break;
+    case 2: k_loop(std::integral_constant<int, 2>{}); break;
+    case 3: k_loop(std::integral_constant<int, 3>{}); break;
+    default: k_loop(std::integral_constant<int, 4>{}); break;
   }
-  if (t < nkt) step(sa0, sa1, sb0, sb2, t);
-  if (t + 1 < nkt) step(sa1, sa0, sb1, sb0, t + 1);
-  if (t + 2 < nkt) step(sa0, sa1, sb2, sb1, t + 2);
-  if (t + 3 < nkt) step(sa1, sa0, sb0, sb2, t + 3);
-  if (t + 4 < nkt) step(sa0, sa1, sb1, sb0, t + 4);
-  // no load may still be writing LDS when the block ends
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
   const int col32 = lane & 31;
   uint16_t* out = (uint16_t*)p.C;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if (!sub_ok[j]) continue;
+    if (j >= nj) continue;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 32 * (wm + 2 * j) + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
