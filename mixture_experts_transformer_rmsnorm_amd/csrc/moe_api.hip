@@ -479,7 +479,8 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
       return nt(act_s, Is, shared_down, shared_down, Is, d, sh_dn, d, Is, kMaxSharedSplits);
     });
   };
-  if (has_shared && !mfma && err == hipSuccess) {
+  auto fork_shared = [&] {
+    if (!has_shared || err != hipSuccess) return;
     slock.lock();
     side = side_stream(p);
     if (side) {
@@ -492,7 +493,8 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
     } else {
       slock.unlock();
     }
-  }
+  };
+  if (!mfma) fork_shared();
   stage(kStRouter,
         [&] { return nt(h, d, router_w, router_w, d, E, logits, E, d, kMaxRouterSplits); });
   // Small batches: per-token selection blocks, then the whole permutation in one
