@@ -249,75 +249,96 @@ hipError_t launch_topk_small(const float* logit_part, int splits, const float* c
   return hipGetLastError();
 }
 
+// Inclusive scan of v over the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
 // Permutation for small batches (T * k <= kRouteSmallMax assignments, one block
-// of 1024 threads): per-expert counts (LDS atomics), then what scan_experts_kernel
-// writes (offsets, active list, M-tiles, pass prefix, header), then each
-// assignment's row: its expert's offset plus the number of earlier assignments,
-// in (token, j) order, of the same expert.  The same stable order as the chunked
-// scatter.
+// of 1024 threads).  The assignments, in (token, j) order, are cut into 16 equal
+// segments; per-segment expert histograms (LDS atomics) give each expert's count
+// and, per segment, the count of the same expert's assignments in the segments
+// before it.  Then what scan_experts_kernel writes (offsets, active list,
+// M-tiles, pass prefix, header) from wave-level scans, and each assignment's row:
+// its expert's offset, plus the count before its segment, plus the earlier
+// assignments of the same expert inside the segment.  The same stable order as
+// the chunked scatter.
 __global__ __launch_bounds__(1024) void route_small_kernel(
     const int32_t* __restrict__ topk_idx, int A, int E, int k, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, RouteHeader* __restrict__ hdr, int32_t* __restrict__ active,
     int2* __restrict__ mtiles, int32_t* __restrict__ pass_base, int32_t* __restrict__ perm_token,
     int32_t* __restrict__ row_of) {
-  __shared__ __attribute__((aligned(16))) int s_idx[kRouteSmallMax];
-  __shared__ int s_cnt[1024], s_act[1024], s_til[1024], s_pas[1024], s_off[1024];
-  const int e = threadIdx.x;
+  constexpr int kSegs = 16;
+  __shared__ int s_idx[kRouteSmallMax];
+  __shared__ int s_hist[kSegs * 1024];  // [segment][expert]
+  __shared__ int s_off[1024];
+  __shared__ int s_wsum[kSegs][4];
+  const int e = threadIdx.x, lane = e & (kWave - 1), w = e / kWave;
+  const int seg = (A + kSegs - 1) / kSegs;  // assignments per segment
+  for (int i = e; i < kSegs * E; i += 1024) s_hist[i] = 0;
   for (int i = e; i < A; i += 1024) s_idx[i] = topk_idx[i];
-  for (int i = A + e; i < ((A + 3) & ~3); i += 1024) s_idx[i] = -1;  // pad to a multiple of 4
-  s_cnt[e] = 0;
   __syncthreads();
-  for (int i = e; i < A; i += 1024) atomicAdd(&s_cnt[s_idx[i]], 1);
+  for (int i = e; i < A; i += 1024) atomicAdd(&s_hist[(i / seg) * E + s_idx[i]], 1);
   __syncthreads();
-  const int c = e < E ? s_cnt[e] : 0;
+  // expert e: exclusive prefix over segments, in place, and its count
+  int c = 0;
+  if (e < E) {
+#pragma unroll
+    for (int q = 0; q < kSegs; ++q) {
+      const int v = s_hist[q * E + e];
+      s_hist[q * E + e] = c;
+      c += v;
+    }
+  }
   const int a = c > 0 ? 1 : 0;
   const int tl = (c + kGroupBM - 1) / kGroupBM;
   const int np = (c + kStreamMaxMT - 1) / kStreamMaxMT;
-  s_act[e] = a;
-  s_til[e] = tl;
-  s_pas[e] = np;
-  for (int off = 1; off < 1024; off <<= 1) {
-    __syncthreads();
-    const int pc = e >= off ? s_cnt[e - off] : 0;
-    const int pa = e >= off ? s_act[e - off] : 0;
-    const int pt = e >= off ? s_til[e - off] : 0;
-    const int pp = e >= off ? s_pas[e - off] : 0;
-    __syncthreads();
-    s_cnt[e] += pc;
-    s_act[e] += pa;
-    s_til[e] += pt;
-    s_pas[e] += pp;
+  // block-wide inclusive scans of (c, a, tl, np) over experts: per wave, then
+  // the totals of the waves before
+  int ic = wave_incl_scan(c, lane), ia = wave_incl_scan(a, lane);
+  int it = wave_incl_scan(tl, lane), ip = wave_incl_scan(np, lane);
+  if (lane == kWave - 1) {
+    s_wsum[w][0] = ic;
+    s_wsum[w][1] = ia;
+    s_wsum[w][2] = it;
+    s_wsum[w][3] = ip;
   }
   __syncthreads();
-  s_off[e] = s_cnt[e] - c;
+  for (int q = 0; q < w; ++q) {
+    ic += s_wsum[q][0];
+    ia += s_wsum[q][1];
+    it += s_wsum[q][2];
+    ip += s_wsum[q][3];
+  }
+  s_off[e] = ic - c;
   if (e < E) {
     counts[e] = c;
-    offsets[e] = s_cnt[e] - c;
+    offsets[e] = ic - c;
     if (a) {
-      active[s_act[e] - 1] = e;
-      pass_base[s_act[e] - 1] = s_pas[e] - np;
+      active[ia - 1] = e;
+      pass_base[ia - 1] = ip - np;
     }
-    const int t0 = s_til[e] - tl;
+    const int t0 = it - tl;
     for (int i = 0; i < tl; ++i) mtiles[t0 + i] = make_int2(e, i * kGroupBM);
   }
   if (e == E - 1) {
-    offsets[E] = s_cnt[e];
-    hdr->n_active = s_act[e];
-    hdr->n_mtiles = s_til[e];
-    hdr->n_passes = s_pas[e];
-    pass_base[s_act[e]] = s_pas[e];
+    offsets[E] = ic;
+    hdr->n_active = ia;
+    hdr->n_mtiles = it;
+    hdr->n_passes = ip;
+    pass_base[ia] = ip;
   }
   __syncthreads();
   for (int i = e; i < A; i += 1024) {
     const int x = s_idx[i];
-    int rank = 0;
-    const int4* p4 = reinterpret_cast<const int4*>(s_idx);
-    const int full = i / 4;
-    for (int j = 0; j < full; ++j) {
-      const int4 v = p4[j];
-      rank += (v.x == x) + (v.y == x) + (v.z == x) + (v.w == x);
-    }
-    for (int j = full * 4; j < i; ++j) rank += s_idx[j] == x;
+    const int q = i / seg;
+    int rank = s_hist[q * E + x];
+    for (int j = q * seg; j < i; ++j) rank += s_idx[j] == x;
     const int row = s_off[x] + rank;
     perm_token[row] = i / k;
     row_of[i] = row;
