@@ -18,12 +18,12 @@
 //
 // Balance.  The launch's work is the list of items (active expert i, pass p,
 // strip s) in that order, a pass being up to kStreamMaxMT of the expert's tokens,
-// each item cut into K / kRsChunk chunks of kRsChunk weight rows.  When there are
-// no more items than resident blocks, block b takes item b whole.  Otherwise the P
-// resident blocks split the chunk list into equal contiguous ranges, lo(b) =
-// floor(b * total / P), so every block reads the same number of weight bytes and
-// the launch ends without a tail of lone blocks (the Stream-K decomposition of
-// Osama et al., 2023, applied to a memory-bound product).  An item whose chunks
+// each item cut into K / kRsChunk chunks of kRsChunk weight rows.  When the items
+// fill at least half of the resident blocks, blocks take whole items (RsGeom).
+// Otherwise the P resident blocks split the chunk list into equal contiguous
+// ranges, lo(b) = floor(b * total / P), so every block reads the same number of
+// weight bytes and the launch ends without a tail of lone blocks (the Stream-K
+// decomposition of Osama et al., 2023, applied to a memory-bound product).  An item whose chunks
 // fall in several blocks leaves one fp32 partial sum per part in a slot, and a
 // small fixup kernel launched right after adds the parts in block order and
 // applies the epilogue; the kernel boundary orders the two, so no block ever
@@ -50,21 +50,34 @@ __host__ __device__ constexpr int rs_strip_cols() {
   return (GU ? rs_threads<GU>() / 2 : rs_threads<GU>()) * (16 / (int)sizeof(T));
 }
 
-// Equal split of `total` chunks over `blocks` blocks.
+// Split of `total` chunks (items of C chunks each) over `blocks` blocks: blocks
+// [0, hblocks) take one whole item each; blocks [hblocks, blocks) split the
+// remaining chunks into equal contiguous ranges, lo(b) = head + floor((b -
+// hblocks) * (total - head) / (blocks - hblocks)).
 struct RsRange {
-  int64_t total;
-  int blocks;
-  __device__ __forceinline__ int64_t lo(int b) const { return (int64_t)b * total / blocks; }
+  int64_t total, C;
+  int blocks, hblocks;
+  __device__ __forceinline__ int64_t lo(int b) const {
+    if (b <= hblocks) return (int64_t)b * C;
+    const int64_t head = (int64_t)hblocks * C;
+    return head + (int64_t)(b - hblocks) * (total - head) / (blocks - hblocks);
+  }
   // The block whose range holds chunk x: the largest b with lo(b) <= x.
   __device__ __forceinline__ int block_of(int64_t x) const {
-    int b = (int)min<int64_t>(blocks - 1, x * blocks / total);
+    const int64_t head = (int64_t)hblocks * C;
+    if (x < head) return (int)(x / C);
+    const int tb = blocks - hblocks;
+    int b = hblocks + (int)min<int64_t>(tb - 1, (x - head) * tb / (total - head));
     while (b + 1 < blocks && lo(b + 1) <= x) ++b;
     while (lo(b) > x) --b;
     return b;
   }
 };
 
-// Geometry of one launch, the same in the main and the fixup kernel.
+// Geometry of one launch, the same in the main and the fixup kernel.  With P
+// resident blocks and n items: P/2 <= n <= P, block b < n takes item b whole
+// (enough blocks to keep HBM busy, no item split); otherwise (few items, or more
+// than P) equal chunk ranges over the P blocks.
 template <typename T, bool GU>
 struct RsGeom {
   int K, n_out, strips, C;
@@ -78,8 +91,13 @@ struct RsGeom {
     C = K / kRsChunk;
     const int64_t items = (int64_t)n_passes * strips;
     R.total = items * C;
-    // With no more items than blocks each block takes one whole item (no cuts).
-    R.blocks = items <= blocks ? (int)max<int64_t>(items, 1) : blocks;
+    R.C = C;
+    if (items > blocks || 2 * items < (int64_t)blocks) {
+      R.hblocks = 0;
+      R.blocks = blocks;
+    } else {
+      R.hblocks = R.blocks = (int)items;
+    }
   }
 };
 
@@ -260,12 +278,13 @@ __device__ __forceinline__ void rs_store(const float (&acc)[MT][Elem<T>::kVec], 
   }
 }
 
-// Slot of block b's part of an item starting at chunk item0: 0 when the part
-// starts the block's range, else 1 (the part then ends the range).
+// Row 0 of the slot of block b's part of an item starting at chunk item0: slot
+// 2b when the part starts the block's range, else 2b + 1 (the part then ends the
+// range).  A slot holds kStreamMaxMT rows of ld floats, one after the other.
 __device__ __forceinline__ float* rs_slot(const StreamFix& fx, const RsRange& R, int b,
-                                          int64_t item0) {
+                                          int64_t item0, int64_t ld) {
   const int sl = item0 > R.lo(b) ? 1 : 0;
-  return fx.parts + ((int64_t)b * 2 + sl) * fx.slot_floats;
+  return fx.parts + ((int64_t)b * 2 + sl) * kStreamMaxMT * ld;
 }
 
 template <typename T, bool GU, int MT>
@@ -283,8 +302,8 @@ __device__ __forceinline__ void rs_part(const GroupArgs& g, const StreamFix& fx,
     return;
   }
   if (!ln.ok) return;
-  float* mine = rs_slot(fx, G.R, b, item0);
   const int64_t ld = rs_slot_ld<T, GU>(G.n_out);
+  float* mine = rs_slot(fx, G.R, b, item0, ld);
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     if (m >= it.mt) break;
@@ -344,14 +363,15 @@ __device__ __forceinline__ void rs_finish(const GroupArgs& g, const StreamFix& f
   if (ln.ok) {
     for (int bb = b; bb <= bl; ++bb) {
       if (G.R.lo(bb) == G.R.lo(bb + 1)) continue;  // empty range
-      const float* src = rs_slot(fx, G.R, bb, item0);
+      const float* src = rs_slot(fx, G.R, bb, item0, ld);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (m >= it.mt) break;
 #pragma unroll
         for (int c = 0; c < V; c += 4) {
           const float4 v =
-              *reinterpret_cast<const float4*>(src + m * ld + ln.spos + (c / 4) * ln.sgap);
+              *reinterpret_cast<const float4*>(src + m * ld + ln.spos +
+                                               (c / 4) * ln.sgap);
           acc[m][c] += v.x;
           acc[m][c + 1] += v.y;
           acc[m][c + 2] += v.z;
@@ -392,6 +412,11 @@ __global__ __launch_bounds__(rs_threads<GU>()) void stream_fixup_kernel(GroupArg
 #undef MOE_FIN
 }
 
+// The partition assumes one block per compute unit (the dispatcher spreads the
+// blocks of a launch over the CUs only when no CU can hold two), so each launch
+// asks for more dynamic LDS than half a CU's 160 KiB; the kernels do not use it.
+constexpr size_t kRsLdsHold = 96 * 1024;
+
 // Blocks of stream_kernel<T, GU> resident on the current device at once (all
 // compute units), capped at kStreamMaxBlocks; queried once per device.
 template <typename T, bool GU>
@@ -407,7 +432,7 @@ static hipError_t resident_blocks(int* blocks) {
     err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
     err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stream_kernel<T, GU>,
-                                                       rs_threads<GU>(), 0);
+                                                       rs_threads<GU>(), kRsLdsHold);
     if (err != hipSuccess) return err;
     n = std::max(1, std::min(kStreamMaxBlocks, std::max(per_cu, 1) * std::max(cus, 1)));
     cached[dev].store(n, std::memory_order_relaxed);
@@ -424,7 +449,7 @@ static hipError_t launch_stream(const GroupArgs& g, const StreamFix& fx_in, cons
   if (err != hipSuccess) return err;
   if (fx.blocks < 1 || fx.blocks > kStreamMaxBlocks || g.E > kMaxStreamExperts)
     return hipErrorInvalidValue;
-  stream_kernel<T, GU><<<dim3((unsigned)fx.blocks), rs_threads<GU>(), 0, s>>>(
+  stream_kernel<T, GU><<<dim3((unsigned)fx.blocks), rs_threads<GU>(), kRsLdsHold, s>>>(
       g, fx, (const T*)A, (const T*)W, (T*)out);
   err = hipGetLastError();
   if (err != hipSuccess || fx.blocks == 1) return err;
