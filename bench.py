@@ -256,6 +256,33 @@ def measure_dense(launches):
     return out
 
 
+def measure_sweep(cfg, tin, steps, warmup, tokens=(1, 8, 16, 32, 128, 256)):
+    """The MoE block at other batch sizes on the same weights (decode-sized batches use
+    the streaming kernels): ms per step, tokens/s and the gate_up kernel's HBM rate."""
+    import torch
+    import workloads
+    out = {}
+    for T in tokens:
+        c = workloads.config(cfg, T=T)
+        t2 = dict(tin)
+        sm = workloads.draw_small(c, 0)
+        for key in ("x", "norm_w", "router_w"):
+            t2[key] = workloads.host_to_torch(sm[key], c.dtype, "cuda")
+        t2["corr_bias"] = torch.from_numpy(sm["corr_bias"]).cuda()
+        r = run_workload(c, t2, steps, warmup)
+        out["T%d" % T] = {"tokens": T, "ms_per_step": round(r["ms_per_step"], 4),
+                          "tokens_per_s": round(r["value"], 1),
+                          "kernel_path": "stream" if r["path"] == 1 else "mfma",
+                          "gate_up_ms": r["roofline"]["kernel_ms"],
+                          "gate_up_" + r["roofline"]["unit"].replace("/", "_per_"):
+                              r["roofline"]["achieved"],
+                          "gate_up_frac": r["roofline"]["frac"],
+                          "active_experts": r["roofline"]["active_experts"]}
+        log("sweep T=%d: %.4f ms/step, %.1f tokens/s" % (T, r["ms_per_step"], r["value"]))
+        del t2
+    return out
+
+
 def measure_pack(launches, experts=32):
     """Expert layout conversion (moe_pack_expert / moe_unpack_expert) at the GLM-5 expert
     shape (d 6144, I 2048, bf16): HBM roofline with algorithmic bytes = each expert's
@@ -312,9 +339,10 @@ def main():
                     help="second workload of the same shape family reported in the line ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--extras", default="norms,dense,pack",
-                    help="comma list of extra entry points measured into the line's 'extras' "
-                         "('norms', 'dense', 'pack'; '' = none)")
+    ap.add_argument("--extras", default="norms,dense,pack,sweep",
+                    help="comma list of extra measurements put into the line's 'extras' "
+                         "('norms', 'dense', 'pack', 'sweep': the block at other batch "
+                         "sizes on the headline weights; '' = none)")
     ap.add_argument("--only-extras", action="store_true",
                     help="measure only the extras and print them as one JSON line (profiling)")
     ap.add_argument("--calib-mib", type=int, default=0,
@@ -341,8 +369,10 @@ def main():
         del src, dst
     extras_req = [e for e in args.extras.split(",") if e]
 
-    def run_extras():
+    def run_extras(cfg=None, tin=None):
         ext = {}
+        if "sweep" in extras_req and tin is not None:
+            ext["batch_sweep"] = measure_sweep(cfg, tin, max(args.steps // 5, 5), 2)
         if "norms" in extras_req:
             ext["rmsnorm"] = measure_norms(max(args.steps // 2, 5))
         if "dense" in extras_req:
@@ -399,7 +429,7 @@ def main():
                                  "stage_ms": r2["stage_ms"]}
             del tin2
     if extras_req:
-        line["extras"] = run_extras()
+        line["extras"] = run_extras(cfg, tin)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, tin, small, args.cpu_seconds)
     print(json.dumps(line), flush=True)

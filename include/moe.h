@@ -91,9 +91,9 @@ typedef enum {
 typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
 
 /* Kernel family for the expert matmuls.
- *  AUTO:   STREAM when the mean tokens per routed expert is small (decode-sized
- *          batches, where the expert weights are streamed once from HBM), MFMA
- *          otherwise.  fp32 plans always use STREAM.
+ *  AUTO:   STREAM when the mean tokens per routed expert, T*k/E, is at most 5
+ *          (decode-sized batches, where the expert weights are streamed once from
+ *          HBM), MFMA otherwise.  fp32 plans always use STREAM.
  *  STREAM: weight-streaming FMA kernels (any dtype).
  *  MFMA:   LDS-tiled bf16 matrix-core kernels (bf16 only).
  *  FUSED:  reserved for a single persistent decode kernel; not available in this

@@ -22,8 +22,9 @@ constexpr size_t kAlign = 256;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 1024;
 // Decode-sized batches (mean tokens per routed expert at most this) take the
-// weight-streaming kernels under MOE_PATH_AUTO.
-constexpr int kStreamMaxMeanTokens = 8;
+// weight-streaming kernels under MOE_PATH_AUTO.  At the GLM-5 shape the streaming
+// path is faster up to 128 tokens (4 per expert) and the MFMA path from 192 (6).
+constexpr int kStreamMaxMeanTokens = 5;
 // Split-K target: enough blocks for two per compute unit on 256 CUs.
 constexpr int kTargetBlocks = 512;
 // Partial sums the router top-k and the shared-expert consumers add per value.
