@@ -27,6 +27,7 @@ constexpr int kMaxExperts = 1024;
 constexpr int kStreamMaxMeanTokens = 5;
 // Split-K target: enough blocks for two per compute unit on 256 CUs.
 constexpr int kTargetBlocks = 512;
+constexpr int kComputeUnits = 256;  // MI355X
 // Partial sums the router top-k and the shared-expert consumers add per value.
 constexpr int kMaxRouterSplits = 16;
 constexpr int kMaxSharedSplits = 16;
@@ -62,14 +63,27 @@ struct Split {
 };
 
 // Split-K factor for a dense K-contiguous product of M rows, N columns, K depth:
-// enough blocks to fill the chip, at least two K tiles per split, at most
-// max_splits partial sums for the consumer to add.
+// at least two K tiles per split and at most max_splits partial sums for the
+// consumer to add.  The 128-row kernel asks for about kTargetBlocks blocks.  The
+// 256-row kernel holds a compute unit alone: with fewer tiles than compute
+// units it splits K to fill one wave of them; with more it splits in two only
+// when that shortens the last, partly filled wave (the partial sums cost HBM
+// traffic, so no further).
 Split nt_split(int64_t M, int64_t N, int64_t K, int tm, int tn, int tk, int max_splits) {
-  const int64_t tiles = cdiv(M, tm) * cdiv(N, tn);
+  const int64_t tiles = std::max<int64_t>(1, cdiv(M, tm) * cdiv(N, tn));
   const int64_t nkt = K / tk;
-  int64_t s = std::max<int64_t>(1, cdiv(kTargetBlocks, std::max<int64_t>(tiles, 1)));
-  s = std::min<int64_t>(s, std::max<int64_t>(1, nkt / 2));
-  s = std::min<int64_t>(s, max_splits);
+  const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(max_splits, nkt / 2));
+  int64_t s = 1;
+  if (tm == kNtBigTile) {
+    if (tiles < kComputeUnits) {
+      s = std::min<int64_t>(smax, cdiv(kComputeUnits, tiles));
+    } else if (smax >= 2 &&
+               10 * cdiv(2 * tiles, kComputeUnits) < 18 * cdiv(tiles, kComputeUnits)) {
+      s = 2;  // waves of half the work, at least 10 % less in all
+    }
+  } else {
+    s = std::min<int64_t>(smax, std::max<int64_t>(1, cdiv(kTargetBlocks, tiles)));
+  }
   const int64_t per = cdiv(nkt, s);
   return Split{(int)cdiv(nkt, per), (int)per};
 }
