@@ -106,6 +106,15 @@ def test_glm5_decode_stream(glm5_weights):
     _check(cfg, glm5_weights, path=moe.MOE_PATH_STREAM)
 
 
+@pytest.mark.parametrize("T", [1, 8])
+def test_glm5_decode_small_batches(glm5_weights, T):
+    """1 and 8 tokens: fewer (expert, pass) items than half the resident blocks, so
+    the streaming kernels split every item over several blocks (equal ranges) and
+    the fixup kernel finishes them all."""
+    cfg = workloads.config("glm5_decode", T=T)
+    _check(cfg, glm5_weights, path=moe.MOE_PATH_AUTO)
+
+
 def test_glm5_stream_split_items(glm5_weights):
     """256 tokens on the streaming path: more (expert, pass) items than resident
     blocks, so the balanced launch splits items between blocks and the fixup
