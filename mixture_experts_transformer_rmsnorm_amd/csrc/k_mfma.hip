@@ -397,6 +397,10 @@ __global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p)
     b_src[i] = p.Bg + (int64_t)e * p.b_stride + (int64_t)k * p.ldb + gcol;
   }
   const int64_t b_kstep = (int64_t)GB_K * p.ldb;
+  // Weight loads of gate_up are marked nontemporal (cache-policy bit 1 of the
+  // instruction), which keeps the gathered activation rows in L2 (gate_up 4 %
+  // faster); for down, whose activation tile is small, the plain policy is faster.
+  constexpr int kBAux = EPI == kEpiSwiGLU ? 2 : 0;
   auto issue_a = [&](uint16_t* dst, int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < GB_A_LOADS; ++i)
@@ -408,7 +412,7 @@ __global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p)
 #pragma unroll
     for (int i = 0; i < GB_B_LOADS; ++i)
       __builtin_amdgcn_global_load_lds(b_src[i] + kt * b_kstep,
-                                       (lds_void_t*)(dst + (4 * w + i) * 512), 16, 0, 0);
+                                       (lds_void_t*)(dst + (4 * w + i) * 512), 16, 0, kBAux);
   };
 
   // ---- compute side
@@ -545,25 +549,50 @@ __global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p)
     default: k_loop(std::integral_constant<int, 4>{}); break;
   }
 
+  // ---- epilogue.  Each wave stages one of its 32-row sub-tiles at a time in a
+  // private LDS region (its 32 or 64 columns of the tile, rows padded by 16
+  // bytes so that the two row halves of an accumulator write use different
+  // banks), then stores whole 16-byte vectors of consecutive columns: a row's
+  // piece of the wave is one 128-byte line (down) or half of one (gate_up),
+  // written by 8 or 4 lanes of one instruction.  The stores are nontemporal
+  // (the outputs are read by the next kernel, not by this one): prefill
+  // gate_up and down are 3 % faster than with plain stores, and 16-byte stores
+  // are faster than storing each lane's 2-byte elements.
+  constexpr int OC = EPI == kEpiSwiGLU ? 32 : 64;  // output columns of a wave
+  constexpr int RSE = OC + 8;                       // LDS row stride, elements
+  constexpr int CPR = OC / 8;                       // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                     // rows per store instruction
+  static_assert(4 * 32 * RSE <= GB_B_ELEMS, "four waves' regions fit one B slot");
+  __syncthreads();  // every wave is done with the rings and its loads have landed
+  uint16_t* stage = (w < 4 ? sb0 : sb1) + (w & 3) * 32 * RSE;
   const int col32 = lane & 31;
+  const int c0 = EPI == kEpiSwiGLU ? n_tile * GB_ACT_COLS + wn * 32 : n_tile * GB_N + wn * 64;
   uint16_t* out = (uint16_t*)p.C;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if (j >= nj) continue;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int r = 32 * (wm + 2 * j) + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      if (r >= rows) continue;
-      uint16_t* orow = out + (int64_t)(seg + m0 + r) * p.ldc;
+      const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
       if (EPI == kEpiSwiGLU) {
-        const int c = n_tile * GB_ACT_COLS + wn * 32 + col32;
-        if (c < p.N) orow[c] = (uint16_t)f32_to_bf16_bits(silu(acc[j][0][i]) * acc[j][1][i]);
+        stage[r * RSE + col32] = (uint16_t)f32_to_bf16_bits(silu(acc[j][0][i]) * acc[j][1][i]);
       } else {
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int c = n_tile * GB_N + bcol(f) + col32;
-          if (c < p.N) orow[c] = (uint16_t)f32_to_bf16_bits(acc[j][f][i]);
-        }
+        for (int f = 0; f < 2; ++f)
+          stage[r * RSE + f * 32 + col32] = (uint16_t)f32_to_bf16_bits(acc[j][f][i]);
+      }
+    }
+    // LDS operations of a wave complete in order: the reads below see the writes
+    // above, and the next sub-tile's writes come after these reads.
+#pragma unroll
+    for (int q = 0; q < 32 / RPI; ++q) {
+      const int rr = q * RPI + lane / CPR, ch = lane % CPR;
+      const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * RSE + ch * 8);
+      const int r = 32 * (wm + 2 * j) + rr, c = c0 + ch * 8;
+      if (r < rows && c < p.N) {
+        const u32x4_t t = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(
+            t, reinterpret_cast<u32x4_t*>(out + (int64_t)(seg + m0 + r) * p.ldc + c));
       }
     }
   }

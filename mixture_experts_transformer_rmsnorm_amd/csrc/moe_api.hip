@@ -66,21 +66,16 @@ struct Split {
 // at least two K tiles per split and at most max_splits partial sums for the
 // consumer to add.  The 128-row kernel asks for about kTargetBlocks blocks.  The
 // 256-row kernel holds a compute unit alone: with fewer tiles than compute
-// units it splits K to fill one wave of them; with more it splits in two only
-// when that shortens the last, partly filled wave (the partial sums cost HBM
-// traffic, so no further).
+// units it splits K to fill one wave of them, with more it does not split (the
+// partial sums cost HBM traffic twice, in the product and in its consumer: a
+// 384-tile product split in two fills its last wave but the step is slower).
 Split nt_split(int64_t M, int64_t N, int64_t K, int tm, int tn, int tk, int max_splits) {
   const int64_t tiles = std::max<int64_t>(1, cdiv(M, tm) * cdiv(N, tn));
   const int64_t nkt = K / tk;
   const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(max_splits, nkt / 2));
   int64_t s = 1;
   if (tm == kNtBigTile) {
-    if (tiles < kComputeUnits) {
-      s = std::min<int64_t>(smax, cdiv(kComputeUnits, tiles));
-    } else if (smax >= 2 &&
-               10 * cdiv(2 * tiles, kComputeUnits) < 18 * cdiv(tiles, kComputeUnits)) {
-      s = 2;  // waves of half the work, at least 10 % less in all
-    }
+    if (tiles < kComputeUnits) s = std::min<int64_t>(smax, cdiv(kComputeUnits, tiles));
   } else {
     s = std::min<int64_t>(smax, std::max<int64_t>(1, cdiv(kTargetBlocks, tiles)));
   }
