@@ -598,6 +598,155 @@ __global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dense kernel for decode-sized batches (mfma_nt_skinny_kernel): the same
+// product for M <= 64 rows, one 64 x 128 tile (all rows, 128 B-rows) and the K
+// range of split z per block, 4 wavefronts each owning 32 B-rows (the columns of
+// the output) for both 32-row halves.  The product streams B (weights, read
+// once, nontemporal loads) from HBM: both operands move global -> LDS directly
+// through a ring of 6 stages (A 64 x 64 and B 128 x 64 elements each, with the
+// XOR swizzle of the 256-row kernel), so 5 K-steps of loads are in flight per
+// compute unit while one is multiplied.  Rows past M load row M - 1 and B rows
+// past N load row 0 (in bounds; their outputs are not stored), so every stage
+// issues the same 6 loads per thread.  No stage is requested past the split's
+// last K-tile; the last steps, which have fewer stages after them, wait for
+// every load of the wave.
+constexpr int NS_M = kNtSkinnyRows, NS_N = kMfmaBN, NS_K = kMfmaBK, NS_THREADS = 256;
+constexpr int NS_STAGES = 6;
+constexpr int NS_A_ELEMS = NS_M * NS_K, NS_B_ELEMS = NS_N * NS_K;  // 8 and 16 KiB
+constexpr int NS_STAGE_ELEMS = NS_A_ELEMS + NS_B_ELEMS;
+constexpr int NS_LOADS = (NS_A_ELEMS + NS_B_ELEMS) / (NS_THREADS * 8);  // per thread and stage
+static_assert(NS_STAGES * NS_STAGE_ELEMS * 2 <= 160 * 1024, "the ring fits the LDS of a CU");
+static_assert(NS_LOADS == 6 && NS_A_ELEMS == 2 * NS_THREADS * 8, "load assignment below");
+
+// s_waitcnt immediate: at most n (< 64) vector-memory operations of this wave
+// outstanding (vmcnt bits 3:0 and 15:14) and all of its LDS operations completed.
+constexpr int waitcnt_vm_n_lgkm0(int n) { return ((n >> 4) << 14) | 0x0070 | (n & 15); }
+
+// One global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane l's
+// bytes land at LDS byte address lds + 16 l; lds must be the same in every lane.
+// NT marks the load nontemporal.  Written as an asm statement so that the
+// compiler does not track these LDS writes itself: with the ring slot chosen at
+// run time it would otherwise wait for every load in flight before each LDS
+// read; the kernel's own waits order them.  The instruction has no result
+// registers (it writes LDS only); M0 is set in the same statement, one wait
+// state ahead of its use.
+template <bool NT>
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  if constexpr (NT)
+    __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                     :
+                     : "v"(src), "s"(lds)
+                     : "memory", "m0");
+  else
+    __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :
+                     : "v"(src), "s"(lds)
+                     : "memory", "m0");
+}
+
+__global__ __launch_bounds__(NS_THREADS) void mfma_nt_skinny_kernel(NtArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[NS_STAGES * NS_STAGE_ELEMS];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_tiles = (a.N + NS_N - 1) / NS_N;
+  const int n_tile = blockIdx.x % n_tiles, z = blockIdx.x / n_tiles;
+  const int nkt = a.K / NS_K;
+  const int kt0 = z * a.k_tiles_per_split;
+  const int kt1 = min(nkt, kt0 + a.k_tiles_per_split);
+  if (kt0 >= kt1) return;
+  const int n0 = n_tile * NS_N;
+  const uint16_t* A = (const uint16_t*)a.A;
+  const uint16_t* B1 = (const uint16_t*)a.B1;
+  const uint16_t* B2 = (const uint16_t*)a.B2;
+
+  // Load side: instruction i of wave w fills the 8 rows 8 (w + 4i) .. +7 of the
+  // A part (i < 2) or of the B part (i < 4), lane / 8 picking the row and
+  // lane % 8 the chunk position; row r's k-chunk c sits at position
+  // c ^ ((r >> 1) & 7) of its 128-byte LDS row.
+  const uint16_t* a_src[2];
+  const uint16_t* b_src[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * (w + 4 * i) + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    a_src[i] = A + (int64_t)min(r, a.M - 1) * a.lda + c * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * (w + 4 * i) + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int n = n0 + r < a.N ? n0 + r : 0;
+    const uint16_t* brow = n < a.n_split ? B1 + (int64_t)n * a.ldb : B2 + (int64_t)(n - a.n_split) * a.ldb;
+    b_src[i] = brow + c * 8;
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)lds;
+  // Stage of K-tile kt into ring slot q.
+  auto issue = [&](int kt, int q) __attribute__((always_inline)) {
+    const int k0 = kt * NS_K;
+    const uint32_t base = lds_base + (uint32_t)(q * NS_STAGE_ELEMS) * 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lds_dma16<false>(a_src[i] + k0, base + (w + 4 * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lds_dma16<true>(b_src[i] + k0, base + NS_A_ELEMS * 2 + (w + 4 * i) * 1024);
+  };
+
+  // Compute side: A fragment of rows 32 j + lane % 32, B fragment of B-rows
+  // 32 w + lane % 32, both at k-chunk 2 ks + lane / 32.
+  const int ra = lane & 31, rb = 32 * w + (lane & 31);
+  f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
+
+  // Step kt: wait until only the loads of the stages after kt are outstanding
+  // (all of them while fewer than 4 follow), barrier (every wave's stage kt has
+  // landed and every wave is done with the slot of step kt - 1), refill that
+  // slot with stage kt + 5, multiply stage kt.
+  int q = 0;  // slot of step kt
+#pragma unroll
+  for (int s = 0; s < NS_STAGES - 1; ++s)
+    if (kt0 + s < kt1) issue(kt0 + s, s);
+  for (int kt = kt0; kt < kt1; ++kt) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + NS_STAGES - 2 < kt1)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_n_lgkm0((NS_STAGES - 2) * NS_LOADS));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_n_lgkm0(0));
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + NS_STAGES - 1 < kt1) issue(kt + NS_STAGES - 1, q == 0 ? NS_STAGES - 1 : q - 1);
+    const uint16_t* as = lds + q * NS_STAGE_ELEMS;
+    const uint16_t* bs = as + NS_A_ELEMS;
+#pragma unroll
+    for (int ks = 0; ks < NS_K / 16; ++ks) {
+      const int ch = 2 * ks + (lane >> 5);
+      const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(bs + rb * NS_K + ((ch ^ ((rb >> 1) & 7)) * 8));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = 32 * j + ra;
+        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(as + r * NS_K + ((ch ^ ((r >> 1) & 7)) * 8));
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b, acc[j], 0, 0, 0);
+      }
+    }
+    q = q == NS_STAGES - 1 ? 0 : q + 1;
+  }
+  // no load may still be writing LDS when the block ends
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_n_lgkm0(0));
+
+  // fp32 partial sums of split z: element i of lane l in a 32x32 tile is row
+  // 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32.
+  float* out = a.out + (int64_t)z * a.M * a.N;
+  const int n = n0 + 32 * w + (lane & 31);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * j + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if (r < a.M && n < a.N) out[(int64_t)r * a.N + n] = acc[j][i];
+    }
+}
+
 hipError_t launch_mfma_nt(const NtArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   MfmaProblem p = {};
@@ -618,6 +767,9 @@ hipError_t launch_mfma_nt(const NtArgs& a, hipStream_t s) {
     const int64_t tiles = (int64_t)((a.M + NB_M - 1) / NB_M) * ((a.N + NB_N - 1) / NB_N) * a.splits;
     const int64_t blocks = (tiles + kXcds - 1) / kXcds * kXcds;
     mfma_nt_big_kernel<<<dim3((unsigned)blocks), NB_THREADS, 0, s>>>(p);
+  } else if (tm == NS_M) {
+    const int64_t blocks = (int64_t)((a.N + NS_N - 1) / NS_N) * a.splits;
+    mfma_nt_skinny_kernel<<<dim3((unsigned)blocks), NS_THREADS, 0, s>>>(a);
   } else {
     dim3 grid((a.N + kNtBN - 1) / kNtBN, (a.M + kNtBM - 1) / kNtBM, a.splits);
     mfma_nt_kernel<<<grid, 256, 0, s>>>(a);

@@ -23,13 +23,15 @@ constexpr int kMfmaBK = 64;
 constexpr int kFmaTile = 32;
 
 // Tile (rows, columns, K-step) of the bf16 dense K-contiguous product for M rows:
-// the direct-to-LDS kernel's 256 x 256 x 64 from 256 rows on, else the
-// register-staged kernel's 128 x 128 x 64.  Host split-K sizing and the launcher
-// both use this, so they agree on the tile.
+// the direct-to-LDS kernel's 256 x 256 x 64 from 256 rows on, the decode-sized
+// direct-to-LDS kernel's 64 x 128 x 64 up to 64 rows, else the register-staged
+// kernel's 128 x 128 x 64.  Host split-K sizing and the launcher both use this,
+// so they agree on the tile.
 constexpr int kNtBigTile = 256;
+constexpr int kNtSkinnyRows = 64;
 inline void mfma_nt_tile(int64_t M, int* tm, int* tn, int* tk) {
-  const bool big = M >= kNtBigTile;
-  *tm = big ? kNtBigTile : kMfmaBM;
+  const bool big = M >= kNtBigTile, skinny = M <= kNtSkinnyRows;
+  *tm = big ? kNtBigTile : skinny ? kNtSkinnyRows : kMfmaBM;
   *tn = big ? kNtBigTile : kMfmaBN;
   *tk = kMfmaBK;
 }

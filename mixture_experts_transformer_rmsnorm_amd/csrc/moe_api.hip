@@ -69,6 +69,10 @@ struct Split {
 // units it splits K to fill one wave of them, with more it does not split (the
 // partial sums cost HBM traffic twice, in the product and in its consumer: a
 // 384-tile product split in two fills its last wave but the step is slower).
+// The 64-row kernel, one block per compute unit too and bound by its weight
+// stream, takes the split count with the fewest K-steps on the busiest compute
+// unit, a split's partial sums (M x 128 fp32 per tile, written and read again)
+// counting as 4M / 64 K-steps of weight traffic spread over all of them.
 Split nt_split(int64_t M, int64_t N, int64_t K, int tm, int tn, int tk, int max_splits) {
   const int64_t tiles = std::max<int64_t>(1, cdiv(M, tm) * cdiv(N, tn));
   const int64_t nkt = K / tk;
@@ -76,6 +80,17 @@ Split nt_split(int64_t M, int64_t N, int64_t K, int tm, int tn, int tk, int max_
   int64_t s = 1;
   if (tm == kNtBigTile) {
     if (tiles < kComputeUnits) s = std::min<int64_t>(smax, cdiv(kComputeUnits, tiles));
+  } else if (tm == kNtSkinnyRows) {
+    double best = 0.0;
+    for (int64_t c = 1; c <= smax; ++c) {
+      const double est = (double)cdiv(tiles * c, kComputeUnits) * (double)cdiv(nkt, c) +
+                         4.0 * (double)std::min<int64_t>(M, tm) / tk * (double)(tiles * c) /
+                             kComputeUnits;
+      if (c == 1 || est < best) {
+        best = est;
+        s = c;
+      }
+    }
   } else {
     s = std::min<int64_t>(smax, std::max<int64_t>(1, cdiv(kTargetBlocks, tiles)));
   }
