@@ -103,6 +103,7 @@ static_assert(NB_TILE_ELEMS == NB_THREADS * 8 * 4, "4 loads per thread and opera
 
 typedef __attribute__((address_space(3))) void lds_void_nt_t;
 
+template <int EPI>
 __global__ __launch_bounds__(NB_THREADS) void mfma_nt_big_kernel(MfmaProblem p) {
   __shared__ __attribute__((aligned(1024))) uint16_t sa0[NB_TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t sa1[NB_TILE_ELEMS];
@@ -116,7 +117,10 @@ __global__ __launch_bounds__(NB_THREADS) void mfma_nt_big_kernel(MfmaProblem p) 
   // N-tile; then the next group; then the split.  The numbers are dealt to the 8
   // XCDs in contiguous ranges, so the 32 blocks an XCD runs at a time cover about
   // 8 M-tiles x 4 N-tiles and share their A and B rows through its L2.
-  const int m_tiles = (p.M + NB_M - 1) / NB_M, n_tiles = (p.N + NB_N - 1) / NB_N;
+  // Output columns of a tile: 256 (fp32 partial sums), or 128 act columns whose
+  // 128 gate and 128 up B-rows the tile multiplies (SwiGLU epilogue).
+  constexpr int NCOLS = EPI == kEpiSwiGLU ? NB_N / 2 : NB_N;
+  const int m_tiles = (p.M + NB_M - 1) / NB_M, n_tiles = (p.N + NCOLS - 1) / NCOLS;
   const int nkt = p.K / NB_K;
   const int splits = (nkt + p.kt_per_split - 1) / p.kt_per_split;
   const int total = m_tiles * n_tiles * splits;
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(NB_THREADS) void mfma_nt_big_kernel(MfmaProblem p) 
   const int lg = l - gm0 * n_tiles;                     // index inside the group
   const int m_tile = gm0 + lg % gsz;
   const int n_tile = lg / gsz;
-  const int m0 = m_tile * NB_M, n0 = n_tile * NB_N;
+  const int m0 = m_tile * NB_M, n0 = n_tile * NCOLS;
   const int rows = min(NB_M, p.M - m0);
   const int kt0 = z * p.kt_per_split;
   const int kt1 = min(nkt, kt0 + p.kt_per_split);
@@ -153,9 +157,14 @@ __global__ __launch_bounds__(NB_THREADS) void mfma_nt_big_kernel(MfmaProblem p) 
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     a_src[i] = p.A + (int64_t)(m0 + min(r, rows - 1)) * p.lda + c * 8;
     a_groups += 8 * (4 * w + i) < rows ? 1 : 0;
-    const int n = n0 + r < p.N ? n0 + r : 0;
-    const uint16_t* brow = n < p.n_split ? p.B1 + (int64_t)n * p.ldb
-                                         : p.B2 + (int64_t)(n - p.n_split) * p.ldb;
+    const uint16_t* brow;
+    if (EPI == kEpiSwiGLU) {  // B-rows [0, 128): gate rows n0 + r; [128, 256): up rows n0 + r - 128
+      const int g = n0 + (r & (NCOLS - 1));
+      brow = (r < NCOLS ? p.B1 : p.B2) + (int64_t)(g < p.N ? g : 0) * p.ldb;
+    } else {
+      const int n = n0 + r < p.N ? n0 + r : 0;
+      brow = n < p.n_split ? p.B1 + (int64_t)n * p.ldb : p.B2 + (int64_t)(n - p.n_split) * p.ldb;
+    }
     b_src[i] = brow + c * 8;
   }
   a_groups = __builtin_amdgcn_readfirstlane(a_groups);
@@ -184,8 +193,11 @@ __global__ __launch_bounds__(NB_THREADS) void mfma_nt_big_kernel(MfmaProblem p) 
 #pragma unroll
     for (int f = 0; f < 2; ++f) acc[j][f] = f32x16_t{};
   const int ar = wm * 32 + (lane & 31);       // A row of sub-tile 0 (sub-tile j: + 64 j)
-  const int br = wn * 64 + (lane & 31);       // B row of column group 0 (group f: + 32 f)
-  const int a_sw = (ar >> 1) & 7, b_sw0 = (br >> 1) & 7, b_sw1 = ((br + 32) >> 1) & 7;
+  // B rows of column groups 0 and 1: 32 adjacent groups of the tile, or (SwiGLU)
+  // the gate rows and the up rows of the wave's 32 act columns.
+  const int br0 = (EPI == kEpiSwiGLU ? wn * 32 : wn * 64) + (lane & 31);
+  const int br1 = br0 + (EPI == kEpiSwiGLU ? NCOLS : 32);
+  const int a_sw = (ar >> 1) & 7, b_sw0 = (br0 >> 1) & 7, b_sw1 = (br1 >> 1) & 7;
 
   // All four sub-tiles are multiplied whatever the row count (rows past the last
   // one hold stale or repeated data and are never stored), so the MFMA stream has
@@ -194,8 +206,8 @@ __global__ __launch_bounds__(NB_THREADS) void mfma_nt_big_kernel(MfmaProblem p) 
     bf16x8_t af[2][4], bf[2][2];
     auto load = [&](int ks, int buf) __attribute__((always_inline)) {
       const int c = 2 * ks + (lane >> 5);
-      bf[buf][0] = *reinterpret_cast<const bf16x8_t*>(bs + br * NB_K + ((c ^ b_sw0) * 8));
-      bf[buf][1] = *reinterpret_cast<const bf16x8_t*>(bs + (br + 32) * NB_K + ((c ^ b_sw1) * 8));
+      bf[buf][0] = *reinterpret_cast<const bf16x8_t*>(bs + br0 * NB_K + ((c ^ b_sw0) * 8));
+      bf[buf][1] = *reinterpret_cast<const bf16x8_t*>(bs + br1 * NB_K + ((c ^ b_sw1) * 8));
       const int a_chunk = (c ^ a_sw) * 8;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -271,18 +283,35 @@ __global__ __launch_bounds__(NB_THREADS) void mfma_nt_big_kernel(MfmaProblem p) 
   }
 
   const int col32 = lane & 31;
-  float* out = (float*)p.C + (int64_t)z * p.M * p.N;
+  if constexpr (EPI == kEpiSwiGLU) {
+    // act[m][n] = silu(gate) * up, bf16, row stride ldc
+    uint16_t* act = (uint16_t*)p.C;
+    const int n = n0 + wn * 32 + col32;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (!sub_ok[j]) continue;
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const int n = n0 + wn * 64 + f * 32 + col32;
-      if (n >= p.N) continue;
+    for (int j = 0; j < 4; ++j) {
+      if (!sub_ok[j] || n >= p.N) continue;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int r = 32 * (wm + 2 * j) + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (r < rows) out[(int64_t)(m0 + r) * p.N + n] = acc[j][f][i];
+        if (r < rows)
+          act[(int64_t)(m0 + r) * p.ldc + n] =
+              (uint16_t)f32_to_bf16_bits(silu(acc[j][0][i]) * acc[j][1][i]);
+      }
+    }
+  } else {
+    float* out = (float*)p.C + (int64_t)z * p.M * p.N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (!sub_ok[j]) continue;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int n = n0 + wn * 64 + f * 32 + col32;
+        if (n >= p.N) continue;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = 32 * (wm + 2 * j) + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          if (r < rows) out[(int64_t)(m0 + r) * p.N + n] = acc[j][f][i];
+        }
       }
     }
   }
@@ -766,7 +795,7 @@ hipError_t launch_mfma_nt(const NtArgs& a, hipStream_t s) {
   if (tm == NB_M) {
     const int64_t tiles = (int64_t)((a.M + NB_M - 1) / NB_M) * ((a.N + NB_N - 1) / NB_N) * a.splits;
     const int64_t blocks = (tiles + kXcds - 1) / kXcds * kXcds;
-    mfma_nt_big_kernel<<<dim3((unsigned)blocks), NB_THREADS, 0, s>>>(p);
+    mfma_nt_big_kernel<kEpiStore><<<dim3((unsigned)blocks), NB_THREADS, 0, s>>>(p);
   } else if (tm == NS_M) {
     const int64_t blocks = (int64_t)((a.N + NS_N - 1) / NS_N) * a.splits;
     mfma_nt_skinny_kernel<<<dim3((unsigned)blocks), NS_THREADS, 0, s>>>(a);
@@ -774,6 +803,28 @@ hipError_t launch_mfma_nt(const NtArgs& a, hipStream_t s) {
     dim3 grid((a.N + kNtBN - 1) / kNtBN, (a.M + kNtBM - 1) / kNtBM, a.splits);
     mfma_nt_kernel<<<grid, 256, 0, s>>>(a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_nt_swiglu(const NtArgs& a, void* act, hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  if (!nt_swiglu_fused(a.M, a.splits) || 2 * a.n_split != a.N) return hipErrorInvalidValue;
+  MfmaProblem p = {};
+  p.A = (const uint16_t*)a.A;
+  p.lda = a.lda;
+  p.B1 = (const uint16_t*)a.B1;
+  p.B2 = (const uint16_t*)a.B2;
+  p.ldb = a.ldb;
+  p.n_split = a.n_split;
+  p.K = a.K;
+  p.N = a.n_split;  // act columns
+  p.M = a.M;
+  p.kt_per_split = a.K / NB_K;
+  p.C = act;
+  p.ldc = a.n_split;
+  const int64_t tiles = (int64_t)((a.M + NB_M - 1) / NB_M) * ((p.N + NB_N / 2 - 1) / (NB_N / 2));
+  const int64_t blocks = (tiles + kXcds - 1) / kXcds * kXcds;
+  mfma_nt_big_kernel<kEpiSwiGLU><<<dim3((unsigned)blocks), NB_THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 

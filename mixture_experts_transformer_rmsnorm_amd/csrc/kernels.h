@@ -79,6 +79,12 @@ struct NtArgs {
 };
 hipError_t launch_fma_nt(int dtype, const NtArgs& a, hipStream_t s);
 hipError_t launch_mfma_nt(const NtArgs& a, hipStream_t s);
+// The gate/up product of a SwiGLU MLP with its epilogue fused (bf16 only, one K
+// split, at least kNtBigTile rows): B rows [0, n_split) are the gate rows (B1)
+// and [n_split, N) the up rows (B2), N = 2 n_split; writes act [M, n_split] bf16
+// = silu(A gate^T) * (A up^T), each element rounded once.
+inline bool nt_swiglu_fused(int64_t M, int splits) { return M >= kNtBigTile && splits == 1; }
+hipError_t launch_mfma_nt_swiglu(const NtArgs& a, void* act, hipStream_t s);
 
 hipError_t launch_topk(const float* logit_part, int splits, const float* corr_bias, int64_t T,
                        int E, int k, float routed_scale, int32_t* topk_idx, float* topk_w,

@@ -494,12 +494,19 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   // routing steps wait for, so it runs in order after the routed experts.
   std::unique_lock<std::mutex> slock(p->smu, std::defer_lock);
   SideStream* side = nullptr;
+  // With one K split the 256-row kernel forms silu(gate) * up itself.
+  const bool fused_act = dt == kBF16 && has_shared && nt_swiglu_fused(T, sgsplit.splits);
   auto shared_branch = [&] {
     stage(kStSharedGateUp, [&] {
+      if (fused_act) {
+        NtArgs a{h, d, shared_gate, shared_up, d, Is, nullptr, (int)T, 2 * Is, d, 1, sgsplit.kt_per};
+        return launch_mfma_nt_swiglu(a, act_s, cs);
+      }
       return nt(h, d, shared_gate, shared_up, d, Is, sh_gu, 2 * (int64_t)Is, d, kMaxSharedSplits);
     });
-    stage(kStSharedAct,
-          [&] { return launch_swiglu_finalize(dt, sh_gu, sgsplit.splits, T, Is, act_s, cs); });
+    if (!fused_act)
+      stage(kStSharedAct,
+            [&] { return launch_swiglu_finalize(dt, sh_gu, sgsplit.splits, T, Is, act_s, cs); });
     stage(kStSharedDown, [&] {
       return nt(act_s, Is, shared_down, shared_down, Is, d, sh_dn, d, Is, kMaxSharedSplits);
     });
@@ -629,8 +636,17 @@ moe_status_t moe_dense_block_forward(moe_plan_t p, void* workspace, size_t works
   };
   // h = RMSNorm(x); act = silu(h gate^T) * (h up^T); out = x + act down^T
   stage(kStNorm, [&] { return launch_rmsnorm(dt, x, d, norm_w, h, d, T, d, c.eps, s); });
-  stage(kStSharedGateUp, [&] { return nt(h, d, gate, up, d, Id, sh_gu, 2 * (int64_t)Id, d, gsplit); });
-  stage(kStSharedAct, [&] { return launch_swiglu_finalize(dt, sh_gu, gsplit.splits, T, Id, act_s, s); });
+  // With one K split the 256-row kernel forms silu(gate) * up itself.
+  const bool fused_act = dt == kBF16 && nt_swiglu_fused(T, gsplit.splits);
+  stage(kStSharedGateUp, [&] {
+    if (fused_act) {
+      NtArgs a{h, d, gate, up, d, Id, nullptr, (int)T, 2 * Id, d, 1, gsplit.kt_per};
+      return launch_mfma_nt_swiglu(a, act_s, s);
+    }
+    return nt(h, d, gate, up, d, Id, sh_gu, 2 * (int64_t)Id, d, gsplit);
+  });
+  if (!fused_act)
+    stage(kStSharedAct, [&] { return launch_swiglu_finalize(dt, sh_gu, gsplit.splits, T, Id, act_s, s); });
   stage(kStSharedDown, [&] { return nt(act_s, Id, down, down, Id, d, sh_dn, d, Id, dsplit); });
   stage(kStCombine, [&] {
     return launch_combine(dt, x, sh_dn, dsplit.splits, nullptr, nullptr, nullptr, T, d, 0, out, s);

@@ -53,6 +53,18 @@ def test_small_dense_blocks(T, d, Id, dtype):
     _check(case, tin, host, g, np.arange(T))
 
 
+def test_dense_fused_swiglu_ragged_width():
+    """Enough 256 x 128 tiles that the gate/up product runs unsplit with its SwiGLU
+    epilogue fused, at an MLP width (1088 = 8.5 x 128) that leaves the last act
+    tile half full; sampled tokens against the oracle."""
+    case = workloads.DenseCase("fused_ragged", 8192, 256, 1088, "bf16")
+    say("dense bf16 T %d d %d Id %d (fused SwiGLU, sampled tokens)" % (case.T, case.d, case.Id))
+    _, tin, host, g = _run(case, case.T, seed=11, weights="host")
+    rng = np.random.default_rng(3)
+    tokens = np.sort(np.concatenate([rng.choice(case.T - 1, size=24, replace=False), [case.T - 1]]))
+    _check(case, tin, host, g, tokens)
+
+
 @pytest.mark.parametrize("name", ["glm5_dense_decode", "glm5_dense_prefill"])
 def test_glm5_dense_block_sampled(name):
     case = workloads.DENSE_CASES[name]
