@@ -262,8 +262,11 @@ MOE_API int32_t moe_plan_path(moe_plan_t plan, int64_t num_tokens, int32_t top_k
  * on (the call's stream, or the side stream for the shared-expert stages);
  * after the caller synchronises, moe_stage_times returns the elapsed
  * milliseconds summed per stage since the last read in ms[stage] and the number
- * of timed calls in *calls.  Timing state is the only mutable part of a plan and
- * is meant for one thread. */
+ * of timed calls in *calls.  A stage whose work another stage's kernel does
+ * records nothing: bf16 shared_act when the shared (or dense) gate/up product
+ * runs at 256 rows or more in one K split and forms silu(gate) * up itself
+ * (its time is in shared_gate_up).  Timing state is the only mutable part of a
+ * plan and is meant for one thread. */
 #define MOE_MAX_STAGES 16
 MOE_API moe_status_t moe_set_stage_timing(moe_plan_t plan, int32_t stage_mask);
 MOE_API moe_status_t moe_stage_times(moe_plan_t plan, double* ms /*[MOE_MAX_STAGES]*/,

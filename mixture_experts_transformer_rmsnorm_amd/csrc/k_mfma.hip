@@ -95,7 +95,10 @@ __global__ __launch_bounds__(256) void mfma_nt_kernel(NtArgs a) {
 // k-chunk c (8 elements) sits at chunk position c ^ ((r >> 1) & 7) of its
 // 128-byte LDS row (chosen on the load side), so the 16-byte fragment reads of
 // 16 consecutive rows hit distinct banks.  A and B fragments are both plain
-// 16-byte LDS reads.
+// 16-byte LDS reads.  Epilogue kEpiStore writes the tile's fp32 partial sums;
+// kEpiSwiGLU (one K split) multiplies 128 gate rows and the matching 128 up rows
+// of B per tile, each wave's two column groups holding the gate and the up sums
+// of the same 32 columns, and writes silu(gate) * up in bf16.
 constexpr int NB_M = kNtBigTile, NB_N = kNtBigTile, NB_K = kMfmaBK, NB_THREADS = 512;
 constexpr int NB_TILE_ELEMS = NB_M * NB_K;  // 32 KiB per operand and slot
 static_assert(5 * NB_TILE_ELEMS * 2 <= 160 * 1024, "rings fit the LDS of a CU");
@@ -659,7 +662,7 @@ constexpr int waitcnt_vm_n_lgkm0(int n) { return ((n >> 4) << 14) | 0x0070 | (n 
 // run time it would otherwise wait for every load in flight before each LDS
 // read; the kernel's own waits order them.  The instruction has no result
 // registers (it writes LDS only); M0 is set in the same statement, one wait
-// state ahead of its use.
+// state ahead of its use, and nothing else in the kernel that calls it uses M0.
 template <bool NT>
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
   if constexpr (NT)
