@@ -256,6 +256,38 @@ def measure_dense(launches):
     return out
 
 
+def measure_configs(cfg, tin, steps, names=("glm5_prefill_zipf", "mid_prefill")):
+    """The MFMA-bound prefill workloads (Zipf-skewed routing at 16384 tokens on the GLM-5
+    weights; the mid-size block at 8192 tokens): tokens/s, the step against the max
+    roofline with its HBM and MFMA fractions, and the dominant kernel's roofline."""
+    import torch
+    import workloads
+    out = {}
+    for name in names:
+        c2 = workloads.config(name)
+        if tin is not None and (c2.d, c2.E, c2.I, c2.Is, c2.dtype) == (cfg.d, cfg.E, cfg.I, cfg.Is, cfg.dtype):
+            t2 = dict(tin)
+            small2 = workloads.draw_small(c2, 0)
+            for key in ("x", "norm_w", "router_w"):
+                t2[key] = workloads.host_to_torch(small2[key], c2.dtype, "cuda")
+            t2["corr_bias"] = torch.from_numpy(small2["corr_bias"]).cuda()
+        else:
+            t2 = workloads.make_torch(c2, 0, device="cuda", weights="device")
+        torch.cuda.synchronize()
+        r = run_workload(c2, t2, steps, 2)
+        out[name] = {"tokens": c2.T, "value": round(r["value"], 1), "unit": "tokens/s",
+                     "ms_per_step": round(r["ms_per_step"], 4),
+                     "kernel_path": "stream" if r["path"] == 1 else "mfma",
+                     "max_expert_load": r["max_load"], "roofline": r["roofline"],
+                     "step_roofline": r["step_roofline"]}
+        log("%s: %.1f tokens/s, %.3f ms/step, step %.1f%% of the max roofline (MFMA %.1f%%)" % (
+            name, r["value"], r["ms_per_step"], 100 * r["step_roofline"]["frac"],
+            100 * r["step_roofline"]["mfma_frac"]))
+        del t2
+        torch.cuda.empty_cache()
+    return out
+
+
 def measure_sweep(cfg, tin, steps, warmup, tokens=(1, 8, 16, 32, 128, 256)):
     """The MoE block at other batch sizes on the same weights (decode-sized batches use
     the streaming kernels): ms per step, tokens/s and the gate_up kernel's HBM rate."""
@@ -339,10 +371,11 @@ def main():
                     help="second workload of the same shape family reported in the line ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--extras", default="norms,dense,pack,sweep",
+    ap.add_argument("--extras", default="norms,dense,pack,sweep,configs",
                     help="comma list of extra measurements put into the line's 'extras' "
                          "('norms', 'dense', 'pack', 'sweep': the block at other batch "
-                         "sizes on the headline weights; '' = none)")
+                         "sizes on the headline weights, 'configs': the MFMA-bound prefill "
+                         "workloads; '' = none)")
     ap.add_argument("--only-extras", action="store_true",
                     help="measure only the extras and print them as one JSON line (profiling)")
     ap.add_argument("--calib-mib", type=int, default=0,
@@ -379,6 +412,8 @@ def main():
             ext["dense_block"] = measure_dense(max(args.steps // 2, 5))
         if "pack" in extras_req:
             ext["expert_pack"] = measure_pack(max(args.steps // 2, 5))
+        if "configs" in extras_req:
+            ext["prefill_configs"] = measure_configs(cfg, tin, max(args.steps // 5, 5))
         return ext
 
     if args.only_extras:
