@@ -361,22 +361,41 @@ __device__ __forceinline__ void rs_finish(const GroupArgs& g, const StreamFix& f
 #pragma unroll
     for (int c = 0; c < V; ++c) acc[m][c] = 0.f;
   if (ln.ok) {
-    for (int bb = b; bb <= bl; ++bb) {
-      if (G.R.lo(bb) == G.R.lo(bb + 1)) continue;  // empty range
-      const float* src = rs_slot(fx, G.R, bb, item0, ld);
+    // The parts of U blocks at a time are loaded together (at one token an item
+    // spans about 32 blocks, and one part after another took a load latency
+    // each), then added in block order; blocks with an empty range hold no part.
+    constexpr int U = 8 / MT;  // 16 float4 of parts in flight per lane
+    for (int bb0 = b; bb0 <= bl; bb0 += U) {
+      float4 v[U][MT][V / 4];
+      bool use[U];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m >= it.mt) break;
+      for (int u = 0; u < U; ++u) {
+        const int bb = bb0 + u;
+        use[u] = bb <= bl && G.R.lo(bb) != G.R.lo(bb + 1);
+        if (use[u]) {
+          const float* src = rs_slot(fx, G.R, bb, item0, ld);
 #pragma unroll
-        for (int c = 0; c < V; c += 4) {
-          const float4 v =
-              *reinterpret_cast<const float4*>(src + m * ld + ln.spos +
-                                               (c / 4) * ln.sgap);
-          acc[m][c] += v.x;
-          acc[m][c + 1] += v.y;
-          acc[m][c + 2] += v.z;
-          acc[m][c + 3] += v.w;
+          for (int m = 0; m < MT; ++m)
+            if (m < it.mt)
+#pragma unroll
+              for (int c = 0; c < V; c += 4)
+                v[u][m][c / 4] = *reinterpret_cast<const float4*>(src + m * ld + ln.spos +
+                                                                  (c / 4) * ln.sgap);
         }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (!use[u]) continue;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          if (m < it.mt)
+#pragma unroll
+            for (int c = 0; c < V; c += 4) {
+              acc[m][c] += v[u][m][c / 4].x;
+              acc[m][c + 1] += v[u][m][c / 4].y;
+              acc[m][c + 2] += v[u][m][c / 4].z;
+              acc[m][c + 3] += v[u][m][c / 4].w;
+            }
       }
     }
   }
