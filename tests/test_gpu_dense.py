@@ -45,7 +45,8 @@ def _check(case, tin, host, g, tokens):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("T,d,Id", [(1, 256, 192), (37, 256, 320), (260, 256, 320), (300, 512, 1024)])
+@pytest.mark.parametrize("T,d,Id", [(1, 256, 192), (37, 256, 320), (63, 512, 704), (64, 512, 704),
+                                    (260, 256, 320), (300, 512, 1024)])
 def test_small_dense_blocks(T, d, Id, dtype):
     case = workloads.DenseCase("small", T, d, Id, dtype)
     say("dense %s T %d d %d Id %d" % (dtype, T, d, Id))
@@ -56,8 +57,9 @@ def test_small_dense_blocks(T, d, Id, dtype):
 def test_dense_fused_swiglu_ragged_width():
     """Enough 256 x 128 tiles that the gate/up product runs unsplit with its SwiGLU
     epilogue fused, at an MLP width (1088 = 8.5 x 128) that leaves the last act
-    tile half full; sampled tokens against the oracle."""
-    case = workloads.DenseCase("fused_ragged", 8192, 256, 1088, "bf16")
+    tile half full and a token count (8000 = 31.25 x 256) that leaves the last
+    row tile a quarter full; sampled tokens (and the last one) against the oracle."""
+    case = workloads.DenseCase("fused_ragged", 8000, 256, 1088, "bf16")
     say("dense bf16 T %d d %d Id %d (fused SwiGLU, sampled tokens)" % (case.T, case.d, case.Id))
     _, tin, host, g = _run(case, case.T, seed=11, weights="host")
     rng = np.random.default_rng(3)
