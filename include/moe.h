@@ -46,13 +46,14 @@
  *  - Ownership: the caller allocates and owns every tensor and the workspace.
  *    The library never allocates device memory, frees, or synchronises inside
  *    moe_block_forward.  A plan's configuration is immutable after creation and
- *    one plan may serve several threads.  A plan also owns, per device, one
- *    non-blocking side stream and two events (made on the first call on that
- *    device that takes the STREAM path with a shared expert, released by
- *    moe_plan_destroy): on that path the shared expert runs there, forked from
- *    and joined back to the call's stream, so the call stays ordered on its
- *    stream (and can be captured into a graph); concurrent calls on one plan
- *    serialise only their host-side enqueueing.
+ *    one plan may serve several threads.  A MoE plan with a shared expert whose
+ *    path is not MFMA also owns one non-blocking side stream and two events on
+ *    the device current at moe_plan_create (made there, released by
+ *    moe_plan_destroy; a forward call creates no HIP object): on the STREAM path
+ *    the shared expert runs there, forked from and joined back to the call's
+ *    stream, so the call stays ordered on its stream (and can be captured into
+ *    a graph); calls on another device run it in order on their own stream.
+ *    Concurrent calls on one plan serialise only their host-side enqueueing.
  *    A workspace serves one call in flight at a time; later calls on the same
  *    stream may reuse it.
  *  - Aliasing: out may alias x (in-place residual); no other aliasing.
@@ -127,6 +128,15 @@ typedef struct moe_plan* moe_plan_t;
  * Returns INVALID_VALUE for null pointers or out-of-range fields,
  * NOT_SUPPORTED for shapes/dtypes/paths the kernels do not handle. */
 MOE_API moe_status_t moe_plan_create(const moe_config_t* cfg, moe_plan_t* plan, size_t* workspace_bytes);
+
+/* Whether a forward call with num_tokens / top_k fits the plan: the host-side
+ * size checks of moe_block_forward (top_k = 0 for a dense-block plan), with no
+ * pointer argument and no device work.  INVALID_VALUE for num_tokens outside
+ * [0, max_tokens] or top_k outside its range; WORKSPACE_TOO_SMALL if a
+ * split-K partial-sum region sized at plan creation could not hold the call's
+ * partial sums (forward calls return the same status before enqueueing
+ * anything); MOE_SUCCESS otherwise. */
+MOE_API moe_status_t moe_plan_check(moe_plan_t plan, int64_t num_tokens, int32_t top_k);
 
 /* Destroy a plan (NULL is accepted). */
 MOE_API moe_status_t moe_plan_destroy(moe_plan_t plan);
@@ -262,7 +272,9 @@ MOE_API int32_t moe_plan_path(moe_plan_t plan, int64_t num_tokens, int32_t top_k
  * on (the call's stream, or the side stream for the shared-expert stages);
  * after the caller synchronises, moe_stage_times returns the elapsed
  * milliseconds summed per stage since the last read in ms[stage] and the number
- * of timed calls in *calls.  A stage whose work another stage's kernel does
+ * of timed calls in *calls.  moe_set_stage_timing makes the events (enough for
+ * 128 calls between two reads; HIP if they cannot be made); a forward call made
+ * while too few are left is neither timed nor counted.  A stage whose work another stage's kernel does
  * records nothing: bf16 shared_act when the shared (or dense) gate/up product
  * runs at 256 rows or more in one K split and forms silu(gate) * up itself
  * (its time is in shared_gate_up).  Timing state is the only mutable part of a

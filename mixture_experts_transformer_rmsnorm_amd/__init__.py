@@ -36,7 +36,8 @@ ABI_VERSION = 1
 EXPORTS = ("moe_plan_create", "moe_plan_destroy", "moe_block_forward", "moe_read_routing",
            "moe_read_buffer", "moe_buffer_bytes", "moe_plan_path", "moe_set_stage_timing",
            "moe_stage_times", "moe_stage_name", "moe_status_string", "moe_abi_version",
-           "moe_rmsnorm", "moe_dense_block_forward", "moe_pack_expert", "moe_unpack_expert")
+           "moe_rmsnorm", "moe_dense_block_forward", "moe_pack_expert", "moe_unpack_expert",
+           "moe_plan_check")
 
 
 class MoEError(RuntimeError):
@@ -81,6 +82,7 @@ def load(path: str = LIB_PATH):
         lib.moe_read_buffer.argtypes = [P, P, P, i64, i32, i32, P, ctypes.c_size_t]
         lib.moe_buffer_bytes.argtypes = [P, i64, i32, i32]
         lib.moe_buffer_bytes.restype = ctypes.c_size_t
+        lib.moe_plan_check.argtypes = [P, i64, i32]
         lib.moe_plan_path.argtypes = [P, i64, i32]
         lib.moe_plan_path.restype = i32
         lib.moe_set_stage_timing.argtypes = [P, i32]
@@ -97,7 +99,8 @@ def load(path: str = LIB_PATH):
         lib.moe_abi_version.restype = i32
         for fn in ("moe_plan_create", "moe_plan_destroy", "moe_block_forward", "moe_read_routing",
                    "moe_read_buffer", "moe_set_stage_timing", "moe_stage_times", "moe_rmsnorm",
-                   "moe_dense_block_forward", "moe_pack_expert", "moe_unpack_expert"):
+                   "moe_dense_block_forward", "moe_pack_expert", "moe_unpack_expert",
+                   "moe_plan_check"):
             getattr(lib, fn).restype = i32
         if lib.moe_abi_version() != ABI_VERSION:
             raise ImportError("libmoe_mi355x.so ABI %d != binding ABI %d"
@@ -249,6 +252,11 @@ def moe_read_buffer(plan, workspace, stream, num_tokens, top_k, which, dst, dst_
                                   which, _ptr(dst), dst_bytes), "moe_read_buffer")
 
 
+def moe_plan_check(plan, num_tokens, top_k) -> None:
+    """Raises MoEError unless a forward call with these sizes fits the plan."""
+    _check(load().moe_plan_check(plan, num_tokens, top_k), "moe_plan_check")
+
+
 def moe_plan_path(plan, num_tokens, top_k) -> int:
     return load().moe_plan_path(plan, num_tokens, top_k)
 
@@ -282,6 +290,41 @@ def moe_stage_times(plan):
 
 
 # ----------------------------------------------------------------------------- convenience
+def _io_tensors(x, out, dim, dtype, device):
+    """x as [T, dim] and out (new, or the caller's) checked against the plan: both
+    contiguous, of the plan's dtype, on the workspace's device, of the same shape."""
+    import torch
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    if x.shape[-1] != dim:
+        raise ValueError("x: last dimension %d, the plan's is %d" % (x.shape[-1], dim))
+    if x.dtype != tdt or x.device != device:
+        raise ValueError("x: %s on %s, the plan needs %s on %s" % (x.dtype, x.device, tdt, device))
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    x2 = x.reshape(-1, dim)
+    if out is None:
+        return x2, torch.empty_like(x2)
+    if out.dtype != tdt or out.device != device or not out.is_contiguous() or \
+            out.numel() != x2.numel():
+        raise ValueError("out must be a contiguous %s tensor on %s with x's %d elements" % (
+            tdt, device, x2.numel()))
+    return x2, out
+
+
+def _check_weights(weights, shapes, dtype, device):
+    """Every named weight present, contiguous, of its shape, dtype and device."""
+    import torch
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    for name, shape in shapes.items():
+        t = weights.get(name)
+        want_dt = torch.float32 if name == "corr_bias" else tdt
+        if t is None or tuple(t.shape) != tuple(shape) or t.dtype != want_dt or \
+                t.device != device or not t.is_contiguous():
+            raise ValueError("weight %s: need a contiguous %s tensor of shape %s on %s, got %s" % (
+                name, want_dt, tuple(shape), device,
+                None if t is None else "%s %s on %s" % (t.dtype, tuple(t.shape), t.device)))
+
+
 class MoEBlock:
     """A plan, its device workspace and the sublayer's weights (torch tensors).
 
@@ -301,6 +344,11 @@ class MoEBlock:
         self.weights = weights
         self.top_k, self.routed_scale = top_k, routed_scale
         self.dim, self.n_experts, self.moe_inter, self.shared_inter = d, E, I2 // 2, Is
+        shapes = {"norm_w": (d,), "router_w": (E, d), "corr_bias": (E,), "gate_up": (E, d, I2),
+                  "down": (E, I2 // 2, d)}
+        if Is:
+            shapes.update(shared_gate=(Is, d), shared_up=(Is, d), shared_down=(d, Is))
+        _check_weights(weights, shapes, self.dtype, gu.device)
         self.cfg = make_config(d, max_tokens, E, I2 // 2, Is, top_k, self.dtype, path, eps)
         self.plan, self.workspace_bytes = moe_plan_create(self.cfg)
         self.workspace = torch.empty(max(self.workspace_bytes, 1), dtype=torch.uint8,
@@ -319,13 +367,8 @@ class MoEBlock:
 
     def forward(self, x, out=None, stream=None):
         """x: [..., d] tensor; returns out of the same shape (may be x itself)."""
-        import torch
         shape = x.shape
-        x2 = x.reshape(-1, self.dim)
-        if not x2.is_contiguous():
-            raise ValueError("x must be contiguous")
-        if out is None:
-            out = torch.empty_like(x2)
+        x2, out = _io_tensors(x, out, self.dim, self.dtype, self.workspace.device)
         w = self.weights
         moe_block_forward(self.plan, self.workspace, self.workspace_bytes, stream, x2.shape[0], x2,
                           w["norm_w"], w["router_w"], w["corr_bias"], w["gate_up"], w["down"],
@@ -371,6 +414,8 @@ class DenseBlock:
         self.dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}[g.dtype]
         self.weights = weights
         self.dim, self.width = d, Id
+        _check_weights(weights, {"norm_w": (d,), "gate": (Id, d), "up": (Id, d), "down": (d, Id)},
+                       self.dtype, g.device)
         self.cfg = make_config(d, max_tokens, 0, 0, Id, 0, self.dtype, MOE_PATH_AUTO, eps)
         self.plan, self.workspace_bytes = moe_plan_create(self.cfg)
         self.workspace = torch.empty(max(self.workspace_bytes, 1), dtype=torch.uint8,
@@ -389,13 +434,8 @@ class DenseBlock:
 
     def forward(self, x, out=None, stream=None):
         """x: [..., d] tensor; returns out of the same shape (may be x itself)."""
-        import torch
         shape = x.shape
-        x2 = x.reshape(-1, self.dim)
-        if not x2.is_contiguous():
-            raise ValueError("x must be contiguous")
-        if out is None:
-            out = torch.empty_like(x2)
+        x2, out = _io_tensors(x, out, self.dim, self.dtype, self.workspace.device)
         w = self.weights
         moe_dense_block_forward(self.plan, self.workspace, self.workspace_bytes, stream, x2.shape[0],
                                 x2, w["norm_w"], w["gate"], w["up"], w["down"], out)

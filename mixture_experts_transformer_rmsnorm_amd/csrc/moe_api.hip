@@ -102,6 +102,8 @@ struct Layout {
   size_t h, logits, topk_idx, topk_w, chunk_cnt, counts, offsets, hdr, active, mtiles,
       perm_token, row_of, pass_base, s_parts, act, y, sh_gu, act_s, sh_dn, sync,
       total;
+  // bytes of the split-K partial-sum regions (router logits, shared gate/up, shared down)
+  size_t logits_bytes, sh_gu_bytes, sh_dn_bytes;
 };
 
 struct EventPair {
@@ -122,14 +124,15 @@ struct moe_plan {
   moe_config_t cfg;
   size_t es;  // bytes per element of D
   Layout lay;
-  // stage timing
+  // stage timing: events are made by moe_set_stage_timing, never by a forward call
   std::mutex tmu;
   int32_t timing_mask = 0;
   int64_t timed_calls = 0;
   std::vector<EventPair> pending;
   std::vector<hipEvent_t> pool;
-  // shared-expert side streams, created on first use per device; smu is held
-  // from a call's fork until its join is enqueued
+  // shared-expert side stream of the device current at plan creation (made there,
+  // never by a forward call); smu is held from a call's fork until its join is
+  // enqueued
   std::mutex smu;
   SideStream side[kMaxSideDevices];
 };
@@ -165,19 +168,26 @@ void nt_tiles(const moe_plan* p, int64_t T, int* tm, int* tn, int* tk) {
   }
 }
 
-// Largest split-K partial buffer (in fp32 elements) over every T <= Tmax.  The split
-// count only changes where the tile count does, at multiples of the row tile (a
-// multiple of 32), so the multiples of 32 and Tmax itself cover every maximum.
+// Largest split-K partial buffer (in fp32 elements) over every T <= Tmax.  The
+// 64-row kernel's split count depends on the row count itself (its estimate
+// counts the partial sums' traffic, 4 min(M, 64) / 64 K-steps per split), and not
+// monotonically, so every T up to kExactRows is evaluated.  From there on the
+// split count depends only on the tile count, which is constant between
+// multiples of the row tile (128 or 256 rows), where the buffer is largest: the
+// multiples of 32 and Tmax itself cover the rest.
+constexpr int64_t kExactRows = 512;
 size_t max_partial_elems(const moe_plan* p, int64_t Tmax, int64_t N, int64_t K, int max_splits) {
   size_t best = 0;
   const int64_t top = std::max<int64_t>(Tmax, 1);
-  for (int64_t T = std::min<int64_t>(32, top);; T = std::min<int64_t>(T + 32, top)) {
+  auto at = [&](int64_t T) {
     int tm, tn, tk;
     nt_tiles(p, T, &tm, &tn, &tk);
     const Split s = nt_split(T, N, K, tm, tn, tk, max_splits);
     best = std::max(best, (size_t)s.splits * (size_t)T * (size_t)N);
-    if (T == top) break;
-  }
+  };
+  for (int64_t T = 1; T <= std::min(top, kExactRows); ++T) at(T);
+  for (int64_t T = kExactRows + 32; T < top; T += 32) at(T);
+  at(top);
   return best;
 }
 
@@ -195,7 +205,8 @@ void make_layout(moe_plan* p) {
   };
   Layout& L = p->lay;
   L.h = take((size_t)T * c.dim * es);
-  L.logits = take(max_partial_elems(p, T, c.n_experts, c.dim, kMaxRouterSplits) * 4);
+  L.logits_bytes = max_partial_elems(p, T, c.n_experts, c.dim, kMaxRouterSplits) * 4;
+  L.logits = take(L.logits_bytes);
   L.topk_idx = take((size_t)A * 4);
   L.topk_w = take((size_t)A * 4);
   L.chunk_cnt = take((size_t)nch * c.n_experts * 4);
@@ -215,48 +226,95 @@ void make_layout(moe_plan* p) {
   L.act = take((size_t)A * c.moe_inter * es);
   L.y = take((size_t)A * c.dim * es);
   if (c.shared_inter > 0) {
-    L.sh_gu = take(max_partial_elems(p, T, 2 * (int64_t)c.shared_inter, c.dim, kMaxSharedSplits) * 4);
+    L.sh_gu_bytes = max_partial_elems(p, T, 2 * (int64_t)c.shared_inter, c.dim, kMaxSharedSplits) * 4;
+    L.sh_gu = take(L.sh_gu_bytes);
     L.act_s = take((size_t)T * c.shared_inter * es);
-    L.sh_dn = take(max_partial_elems(p, T, c.dim, c.shared_inter, kMaxSharedSplits) * 4);
+    L.sh_dn_bytes = max_partial_elems(p, T, c.dim, c.shared_inter, kMaxSharedSplits) * 4;
+    L.sh_dn = take(L.sh_dn_bytes);
   } else {
     L.sh_gu = L.act_s = L.sh_dn = 0;
+    L.sh_gu_bytes = L.sh_dn_bytes = 0;
   }
   L.sync = take((size_t)kFusedSyncWords(std::max(c.n_experts, 1)) * 4);
   L.total = off;
 }
 
+// The split-K partial sums a call of T rows writes fit the regions the plan sized
+// for max_tokens (WORKSPACE_TOO_SMALL otherwise; checked before anything is
+// enqueued, so a sizing mistake can never write past a region).
+moe_status_t check_splits(const moe_plan* p, int64_t T) {
+  const moe_config_t& c = p->cfg;
+  if (T <= 0) return MOE_SUCCESS;
+  int tm, tn, tk;
+  nt_tiles(p, T, &tm, &tn, &tk);
+  auto fits = [&](int64_t N, int64_t K, int max_splits, size_t bytes) {
+    const Split s = nt_split(T, N, K, tm, tn, tk, max_splits);
+    return (size_t)s.splits * (size_t)T * (size_t)N * 4 <= bytes;
+  };
+  if (c.n_experts > 0 && !fits(c.n_experts, c.dim, kMaxRouterSplits, p->lay.logits_bytes))
+    return MOE_ERROR_WORKSPACE_TOO_SMALL;
+  if (c.shared_inter > 0 &&
+      (!fits(2 * (int64_t)c.shared_inter, c.dim, kMaxSharedSplits, p->lay.sh_gu_bytes) ||
+       !fits(c.dim, c.shared_inter, kMaxSharedSplits, p->lay.sh_dn_bytes)))
+    return MOE_ERROR_WORKSPACE_TOO_SMALL;
+  return MOE_SUCCESS;
+}
+
 bool misaligned(const void* ptr) { return ((uintptr_t)ptr & 15u) != 0; }
 
+// Calls whose selected stages the event pool made by moe_set_stage_timing covers
+// (two events per stage and call); a call made while the pool is short is not
+// timed and not counted.
+constexpr int kTimedCallsMax = 128;
+
+int popcount32(uint32_t v) { return __builtin_popcount(v); }
+
 hipEvent_t get_event(moe_plan* p) {
-  if (!p->pool.empty()) {
-    hipEvent_t e = p->pool.back();
-    p->pool.pop_back();
-    return e;
-  }
-  hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (p->pool.empty()) return nullptr;
+  hipEvent_t e = p->pool.back();
+  p->pool.pop_back();
   return e;
 }
 
-// The side stream of the current device (created on first use: non-blocking, at
-// the default priority), or nullptr when it cannot be made; call with smu held.
+// Stage timing of one forward call: returns the selected stages, with the timing
+// state locked until the call returns, or 0 (unlocked) when timing is off or the
+// event pool cannot cover every selected stage of the call.
+int32_t begin_timing(moe_plan* p, std::unique_lock<std::mutex>& lk) {
+  lk = std::unique_lock<std::mutex>(p->tmu);
+  const int32_t m = p->timing_mask;
+  if (m == 0 || p->pool.size() < (size_t)2 * popcount32((uint32_t)m)) {
+    lk.unlock();
+    return 0;
+  }
+  ++p->timed_calls;
+  return m;
+}
+
+// Makes the side stream (non-blocking, at the default priority) and its fork and
+// join events on the current device.  Failure (no device) leaves none: calls then
+// run the shared expert in order on their own stream.
+void make_side_stream(moe_plan* p) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return;
+  SideStream& sd = p->side[dev];
+  hipStream_t st = nullptr;
+  hipEvent_t f = nullptr, j = nullptr;
+  if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return;
+  if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+    if (f) (void)hipEventDestroy(f);
+    (void)hipStreamDestroy(st);
+    return;
+  }
+  sd.stream = st, sd.fork = f, sd.join = j;
+}
+
+// The side stream of the current device, or nullptr when the plan has none there.
 SideStream* side_stream(moe_plan* p) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return nullptr;
   SideStream& sd = p->side[dev];
-  if (!sd.stream) {
-    hipStream_t st = nullptr;
-    hipEvent_t f = nullptr, j = nullptr;
-    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
-      if (f) (void)hipEventDestroy(f);
-      (void)hipStreamDestroy(st);
-      return nullptr;
-    }
-    sd.stream = st, sd.fork = f, sd.join = j;
-  }
-  return &sd;
+  return sd.stream ? &sd : nullptr;
 }
 
 }  // namespace
@@ -310,6 +368,8 @@ moe_status_t moe_plan_create(const moe_config_t* cfg, moe_plan_t* plan, size_t* 
   p->cfg = *cfg;
   p->es = cfg->dtype == MOE_DTYPE_BF16 ? 2 : 4;
   make_layout(p);
+  // the streaming path runs the shared expert on a side stream
+  if (!dense && cfg->shared_inter > 0 && cfg->path != MOE_PATH_MFMA) make_side_stream(p);
   *plan = p;
   *workspace_bytes = p->lay.total;
   return MOE_SUCCESS;
@@ -339,9 +399,25 @@ int32_t moe_plan_path(moe_plan_t p, int64_t num_tokens, int32_t top_k) {
   return use_mfma(p, num_tokens, top_k) ? MOE_PATH_MFMA : MOE_PATH_STREAM;
 }
 
+moe_status_t moe_plan_check(moe_plan_t p, int64_t T, int32_t k) {
+  if (!p) return MOE_ERROR_INVALID_VALUE;
+  const moe_config_t& c = p->cfg;
+  if (T < 0 || T > c.max_tokens) return MOE_ERROR_INVALID_VALUE;
+  if (c.n_experts == 0 ? k != 0 : (k < 1 || k > c.max_top_k || k > c.n_experts))
+    return MOE_ERROR_INVALID_VALUE;
+  return check_splits(p, T);
+}
+
 moe_status_t moe_set_stage_timing(moe_plan_t p, int32_t stage_mask) {
   if (!p || stage_mask < 0 || stage_mask >= (1 << kNumStages)) return MOE_ERROR_INVALID_VALUE;
   std::lock_guard<std::mutex> g(p->tmu);
+  // events for kTimedCallsMax calls, beside those still pending
+  const size_t want = (size_t)2 * popcount32((uint32_t)stage_mask) * kTimedCallsMax;
+  while (p->pool.size() < want) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return MOE_ERROR_HIP;
+    p->pool.push_back(e);
+  }
   p->timing_mask = stage_mask;
   return MOE_SUCCESS;
 }
@@ -387,6 +463,10 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
       (has_shared && (misaligned(shared_gate) || misaligned(shared_up) || misaligned(shared_down))))
     return MOE_ERROR_MISALIGNED;
   if (workspace_bytes < p->lay.total) return MOE_ERROR_WORKSPACE_TOO_SMALL;
+  {
+    const moe_status_t st = check_splits(p, T);
+    if (st != MOE_SUCCESS) return st;
+  }
 
   hipStream_t s = (hipStream_t)stream;
   const Layout& L = p->lay;
@@ -419,16 +499,8 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   int tm, tn, tk;
   nt_tiles(p, T, &tm, &tn, &tk);
 
-  std::unique_lock<std::mutex> tlock(p->tmu, std::defer_lock);
-  int32_t tmask = 0;
-  {
-    std::lock_guard<std::mutex> g(p->tmu);
-    tmask = p->timing_mask;
-  }
-  if (tmask) {
-    tlock.lock();
-    ++p->timed_calls;
-  }
+  std::unique_lock<std::mutex> tlock;
+  const int32_t tmask = begin_timing(p, tlock);
   hipError_t err = hipSuccess;
   hipStream_t cs = s;  // stream the stages below are enqueued on
   auto stage = [&](int st, auto&& fn) {
@@ -587,6 +659,10 @@ moe_status_t moe_dense_block_forward(moe_plan_t p, void* workspace, size_t works
       misaligned(up) || misaligned(down) || misaligned(out))
     return MOE_ERROR_MISALIGNED;
   if (workspace_bytes < p->lay.total) return MOE_ERROR_WORKSPACE_TOO_SMALL;
+  {
+    const moe_status_t st = check_splits(p, T);
+    if (st != MOE_SUCCESS) return st;
+  }
 
   hipStream_t s = (hipStream_t)stream;
   const Layout& L = p->lay;
@@ -607,11 +683,8 @@ moe_status_t moe_dense_block_forward(moe_plan_t p, void* workspace, size_t works
     return dt == kBF16 ? launch_mfma_nt(a, s) : launch_fma_nt(dt, a, s);
   };
 
-  int32_t tmask = 0;
-  std::unique_lock<std::mutex> tlock(p->tmu);
-  tmask = p->timing_mask;
-  if (tmask) ++p->timed_calls;
-  else tlock.unlock();
+  std::unique_lock<std::mutex> tlock;
+  const int32_t tmask = begin_timing(p, tlock);
   hipError_t err = hipSuccess;
   auto stage = [&](int st, auto&& fn) {
     if (err != hipSuccess) return;

@@ -32,15 +32,38 @@ def prepare(cfg, seed=0, weights="host"):
     return cfg, small, route, tin
 
 
+GUARD_BYTES = 1 << 20
+GUARD_BYTE = 0xA5
+
+
+def guard_workspace(block):
+    """Re-seat the block's workspace at the front of a larger buffer whose tail (the
+    guard) holds a fixed byte pattern; returns the guard."""
+    big = torch.full((block.workspace_bytes + GUARD_BYTES,), GUARD_BYTE, dtype=torch.uint8,
+                     device=block.workspace.device)
+    block.workspace = big[:block.workspace_bytes]
+    return big[block.workspace_bytes:]
+
+
+def assert_guard(guard):
+    torch.cuda.synchronize()
+    bad = int((guard != GUARD_BYTE).sum())
+    assert bad == 0, "%d bytes past the workspace were written" % bad
+
+
+def make_block(cfg, tin, path=moe.MOE_PATH_AUTO, max_tokens=None):
+    return moe.MoEBlock({k: tin[k] for k in ("norm_w", "router_w", "corr_bias", "gate_up", "down",
+                                             "shared_gate", "shared_up", "shared_down")
+                         if tin.get(k) is not None},
+                        max_tokens=max(cfg.T if max_tokens is None else max_tokens, 1),
+                        top_k=cfg.k, routed_scale=cfg.routed_scale, eps=cfg.eps, path=path)
+
+
 def run_gpu(cfg, tin, path=moe.MOE_PATH_AUTO, T=None, out=None, x=None, block=None):
     """One forward through moe_block_forward; returns (block, out tensor)."""
     T = cfg.T if T is None else T
     if block is None:
-        block = moe.MoEBlock({k: tin[k] for k in ("norm_w", "router_w", "corr_bias", "gate_up",
-                                                  "down", "shared_gate", "shared_up",
-                                                  "shared_down")},
-                             max_tokens=max(T, 1), top_k=cfg.k, routed_scale=cfg.routed_scale,
-                             eps=cfg.eps, path=path)
+        block = make_block(cfg, tin, path, max_tokens=T)
     x = tin["x"][:T] if x is None else x
     res = block.forward(x, out=out)
     torch.cuda.synchronize()
@@ -199,8 +222,9 @@ def check_delta(got_out, x, delta_ref, dtype):
 def check_outputs(cfg, small, g_out, delta_ref, out_ref, tokens):
     """out against the oracle's exact x + delta (before its own rounding to D, so
     the two sides' independent roundings are not compared with each other), and
-    delta beyond the one rounding of out.  out_ref (the oracle's rounded output)
-    must agree within one unit in the last place."""
+    delta beyond the one rounding of out.  How often the GPU's out differs from the
+    oracle's own rounded out, and by how many units in the last place, is printed
+    as a diagnostic only (near zero an ulp is far below the bar)."""
     x = values(small["x"][tokens], cfg.dtype)
     got = values(g_out, cfg.dtype)
     delta_ref = np.asarray(delta_ref, np.float64)

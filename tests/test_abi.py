@@ -255,3 +255,41 @@ def test_unpack_rejects_outputs_overlapping_inputs():
     # output `up` inside the input gate_up
     assert lib.moe_unpack_expert(0, moe.MOE_DTYPE_BF16, 256, 128, 0x600000, 0x700000, 0x100000,
                                  0x600000 + 1024, 0x300000) == moe.MOE_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("kw", [
+    dict(max_tokens=8), dict(max_tokens=16), dict(max_tokens=64), dict(max_tokens=300),
+    dict(max_tokens=8, path=moe.MOE_PATH_MFMA),
+    dict(dim=4096, n_experts=128, moe_inter=1408, shared_inter=1408, max_tokens=64),
+    dict(dim=2048, moe_inter=1024, shared_inter=1024, max_tokens=40),
+    dict(dtype="f32", dim=256, n_experts=8, moe_inter=128, shared_inter=128, max_top_k=2,
+         max_tokens=100),
+])
+def test_split_partials_fit_every_token_count(kw):
+    """The split-K partial sums of every call size up to max_tokens fit the regions the
+    plan sized (the 64-row kernel's split count is not monotone in the row count, so a
+    plan for 8 tokens called with 7 needs more partial sums than at 8)."""
+    plan, _ = moe.moe_plan_create(_cfg(**kw))
+    try:
+        k = kw.get("max_top_k", 8)
+        for T in range(0, kw["max_tokens"] + 1):
+            moe.moe_plan_check(plan, T, k)
+        with pytest.raises(moe.MoEError) as ei:
+            moe.moe_plan_check(plan, kw["max_tokens"] + 1, k)
+        assert ei.value.status == moe.MOE_ERROR_INVALID_VALUE
+        with pytest.raises(moe.MoEError):
+            moe.moe_plan_check(plan, 1, k + 1)
+    finally:
+        moe.moe_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("max_tokens", [8, 64, 513])
+def test_dense_split_partials_fit_every_token_count(max_tokens):
+    plan, _ = moe.moe_plan_create(_dense_cfg(max_tokens=max_tokens))
+    try:
+        for T in range(0, max_tokens + 1):
+            moe.moe_plan_check(plan, T, 0)
+        with pytest.raises(moe.MoEError):
+            moe.moe_plan_check(plan, 4, 1)
+    finally:
+        moe.moe_plan_destroy(plan)

@@ -1,8 +1,13 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times (one plan per workload, max_tokens = T, MOE_PATH_AUTO unless
 stated).  Routing (selected sets, per-expert counts) is checked on every token;
-outputs on every token for the decode batch and on a seeded, stratified sample
-of tokens (computed one by one by the oracle) for the prefill batches."""
+outputs (out, delta) and the intermediates act and y of every (token, expert)
+pair on every token for the decode batch, and on a seeded, stratified sample of
+512 tokens (computed one by one by the oracle) for the prefill batches: every
+256-row M-tile of the hottest expert, the last M-tile of the 8 busiest, the
+rarest non-empty experts, the first and last token, the rest uniform.  Plans sized
+for more tokens than a call passes are checked too, with a guard region after
+the workspace that must stay untouched."""
 import numpy as np
 import pytest
 import torch
@@ -10,13 +15,15 @@ import torch
 import mixture_experts_transformer_rmsnorm_amd as moe
 import oracle
 import workloads
-from tests.gpu_harness import (check_close, check_outputs, check_permutation, check_routing,
-                               read_all, run_gpu, say, values)
+from tests.gpu_harness import (assert_guard, check_intermediate, check_outputs, check_permutation,
+                               check_routing, guard_workspace, make_block, read_all, run_gpu, say,
+                               values)
 from tests.margin import filtered_small
 
 pytestmark = pytest.mark.gpu
 
-N_SAMPLE = 24
+N_SAMPLE = 512
+M_TILE = 256  # rows per M-tile of the grouped kernels
 
 
 class Weights:
@@ -61,17 +68,39 @@ def _inputs(cfg, weights):
 
 
 def _sample_tokens(cfg, route, n, seed=0):
+    """Stratified token sample.  An expert's segment holds its tokens in token order,
+    so its i-th token sits in M-tile i // 256."""
     rng = np.random.default_rng(seed)
-    picks = set(rng.choice(cfg.T, size=min(n, cfg.T), replace=False).tolist())
     cnt = np.bincount(route["idx"].ravel(), minlength=cfg.E)
-    # stratify: tokens of the hottest expert and of the rarest non-empty experts
-    hot = int(np.argmax(cnt))
-    picks.update(np.nonzero(np.any(route["idx"] == hot, 1))[0][:4].tolist())
-    rare = [e for e in np.argsort(cnt) if cnt[e] > 0][:4]
-    for e in rare:
-        picks.update(np.nonzero(np.any(route["idx"] == e, 1))[0][:1].tolist())
-    picks.add(cfg.T - 1)
+    order = np.argsort(-cnt, kind="stable")
+    picks = {0, cfg.T - 1}
+
+    def tokens_of(e):
+        return np.nonzero(np.any(route["idx"] == e, 1))[0]
+
+    hot = tokens_of(order[0])
+    for m0 in range(0, len(hot), M_TILE):  # every M-tile of the hottest expert
+        picks.add(int(rng.choice(hot[m0:m0 + M_TILE])))
+    for e in order[:8]:  # the last M-tile (and last row) of the 8 busiest experts
+        toks = tokens_of(e)
+        picks.add(int(rng.choice(toks[(len(toks) - 1) // M_TILE * M_TILE:])))
+        picks.add(int(toks[-1]))
+    for e in [e for e in np.argsort(cnt, kind="stable") if cnt[e] > 0][:8]:  # rarest
+        picks.add(int(tokens_of(e)[0]))
+    for t in rng.permutation(cfg.T):
+        if len(picks) >= n:
+            break
+        picks.add(int(t))
     return np.array(sorted(picks), np.int64)
+
+
+def _check_intermediates(cfg, g, tokens, dbg):
+    """act and y of every (token, expert) pair of the listed tokens, read through row_of."""
+    rows = g["row_of"][tokens].ravel()
+    check_intermediate(values(g["act"][rows], cfg.dtype), dbg["act"].reshape(-1, cfg.I),
+                       cfg.dtype, "act")
+    check_intermediate(values(g["y"][rows], cfg.dtype), dbg["y"].reshape(-1, cfg.d), cfg.dtype,
+                       "y")
 
 
 def _check(cfg, weights, path=moe.MOE_PATH_AUTO, n_sample=None):
@@ -91,8 +120,10 @@ def _check(cfg, weights, path=moe.MOE_PATH_AUTO, n_sample=None):
     experts = np.unique(route["idx"][tokens])
     say("  oracle on %d tokens (%d experts)" % (len(tokens), len(experts)))
     gu, dn, sh = weights.host_experts(cfg, experts)
-    delta, out_ref = oracle.experts(tokens, small["x"], route["h"], route["idx"], route["w"], gu,
-                                    dn, sh[0], sh[1], sh[2], oracle.DTYPES[cfg.dtype])
+    delta, out_ref, dbg = oracle.experts(tokens, small["x"], route["h"], route["idx"], route["w"],
+                                         gu, dn, sh[0], sh[1], sh[2], oracle.DTYPES[cfg.dtype],
+                                         debug=True)
+    _check_intermediates(cfg, g, tokens, dbg)
     got = workloads.torch_to_host(out)[tokens]
     check_outputs(cfg, small, got, delta, out_ref, tokens)
     if moe.moe_plan_path(block.plan, cfg.T, cfg.k) == moe.MOE_PATH_FUSED:
@@ -120,7 +151,50 @@ def test_glm5_stream_split_items(glm5_weights):
     blocks, so the balanced launch splits items between blocks and the fixup
     kernel finishes them."""
     cfg = workloads.config("glm5_decode", T=256)
-    _check(cfg, glm5_weights, path=moe.MOE_PATH_STREAM, n_sample=N_SAMPLE)
+    _check(cfg, glm5_weights, path=moe.MOE_PATH_STREAM)
+
+
+def _fewer_tokens_than_planned(cfg, weights, path, max_tokens, calls):
+    """One plan for max_tokens, called with each T in `calls` (smaller): every token's
+    output against the oracle, and nothing written past the workspace."""
+    small, route, tin = _inputs(cfg, weights)
+    block = make_block(cfg, tin, path, max_tokens=max_tokens)
+    guard = guard_workspace(block)
+    for T in calls:
+        say("%s: plan for %d tokens, call with %d (path %d)" % (cfg.name, max_tokens, T,
+                                                                moe.moe_plan_path(block.plan, T, cfg.k)))
+        _, out = run_gpu(cfg, tin, path, T=T, block=block)
+        assert_guard(guard)
+        g = read_all(block, cfg, T)
+        sub = dict(route, idx=route["idx"][:T], w=route["w"][:T], margin=route["margin"][:T])
+        check_routing(g, sub, cfg)
+        tokens = np.arange(T)
+        experts = np.unique(route["idx"][tokens])
+        gu, dn, sh = weights.host_experts(cfg, experts)
+        delta, out_ref, dbg = oracle.experts(tokens, small["x"], route["h"], route["idx"],
+                                             route["w"], gu, dn, sh[0], sh[1], sh[2],
+                                             oracle.DTYPES[cfg.dtype], debug=True)
+        _check_intermediates(cfg, g, tokens, dbg)
+        check_outputs(cfg, small, workloads.torch_to_host(out)[tokens], delta, out_ref, tokens)
+    block.close()
+
+
+def test_glm5_plan_for_8_tokens_called_with_fewer(glm5_weights):
+    """The shared expert's 64-row products pick their K split from the row count, not
+    monotonically: a plan for 8 tokens called with 1..7 (GLM-5 shared-expert sizes)."""
+    cfg = workloads.config("glm5_decode", T=8)
+    _fewer_tokens_than_planned(cfg, glm5_weights, moe.MOE_PATH_AUTO, 8, range(1, 8))
+
+
+@pytest.mark.parametrize("path,max_tokens,calls", [
+    (moe.MOE_PATH_STREAM, 16, (7, 3)),
+    (moe.MOE_PATH_STREAM, 64, (49,)),
+    (moe.MOE_PATH_MFMA, 64, (49, 7)),
+    (moe.MOE_PATH_MFMA, 300, (257, 130)),
+])
+def test_glm5_plan_larger_than_call(glm5_weights, path, max_tokens, calls):
+    cfg = workloads.config("glm5_decode", T=max_tokens)
+    _fewer_tokens_than_planned(cfg, glm5_weights, path, max_tokens, calls)
 
 
 @pytest.mark.skip(reason="the fused decode kernel is switched off: its first GPU run did not "
@@ -132,7 +206,7 @@ def test_glm5_decode_fused(glm5_weights):
 
 def test_glm5_decode_mfma(glm5_weights):
     cfg = workloads.config("glm5_decode")
-    _check(cfg, glm5_weights, path=moe.MOE_PATH_MFMA, n_sample=16)
+    _check(cfg, glm5_weights, path=moe.MOE_PATH_MFMA)
 
 
 def test_glm5_prefill(glm5_weights):
@@ -148,5 +222,8 @@ def test_mid_prefill():
     cfg = workloads.config("mid_prefill")
     w = Weights(cfg)
     _check(cfg, w, n_sample=N_SAMPLE)
+    # plans sized for more tokens than the call, on both kernel families
+    for path in (moe.MOE_PATH_STREAM, moe.MOE_PATH_MFMA):
+        _fewer_tokens_than_planned(workloads.config(cfg, T=64), w, path, 64, (49,))
     del w
     torch.cuda.empty_cache()

@@ -8,7 +8,8 @@ import torch
 import mixture_experts_transformer_rmsnorm_amd as moe
 import oracle
 import workloads
-from tests.gpu_harness import (check_close, check_intermediate, check_outputs, check_permutation, check_routing,
+from tests.gpu_harness import (assert_guard, check_close, check_intermediate, check_outputs,
+                               check_permutation, check_routing, guard_workspace, make_block,
                                oracle_outputs, prepare, read_all, run_gpu, say, values)
 
 pytestmark = pytest.mark.gpu
@@ -128,6 +129,61 @@ def test_smaller_call_after_larger_reuses_workspace():
     assert np.array_equal(g["counts"], cnt)
     delta, out_ref = oracle_outputs(cfg, small, route, tin, np.arange(T2))
     check_outputs(cfg, small, workloads.torch_to_host(out), delta, out_ref, np.arange(T2))
+
+
+@pytest.mark.parametrize("path", [STREAM, MFMA])
+@pytest.mark.parametrize("max_tokens,calls", [(8, (3, 7)), (16, (7,)), (64, (49, 1)), (300, (129,))])
+def test_plan_for_more_tokens_than_the_call(path, max_tokens, calls):
+    """The serving case: a plan sized for the largest batch, called with fewer tokens.
+    At d 2048 with a shared expert of 1024 the 64-row products' split-K counts vary
+    with the row count; a guard region after the workspace must stay untouched."""
+    cfg = workloads.config("tiny_fp32", dtype="bf16", T=max_tokens, d=2048, E=16, I=256,
+                           Is=1024, k=4)
+    cfg, small, route, tin = prepare(cfg, seed=19)
+    block = make_block(cfg, tin, path, max_tokens=max_tokens)
+    guard = guard_workspace(block)
+    for T in calls:
+        say("plan for %d tokens, call with %d, path %d" % (max_tokens, T, path))
+        _, out = run_gpu(cfg, tin, path, T=T, block=block)
+        assert_guard(guard)
+        g = read_all(block, cfg, T)
+        sub = dict(route, idx=route["idx"][:T], w=route["w"][:T], margin=route["margin"][:T])
+        check_routing(g, sub, cfg)
+        check_permutation(g, cfg, T)
+        delta, out_ref, dbg = oracle_outputs(cfg, small, route, tin, np.arange(T), debug=True)
+        rows = g["row_of"].ravel()
+        check_intermediate(values(g["act"][rows], cfg.dtype), dbg["act"].reshape(-1, cfg.I),
+                           cfg.dtype, "act")
+        check_intermediate(values(g["y"][rows], cfg.dtype), dbg["y"].reshape(-1, cfg.d),
+                           cfg.dtype, "y")
+        check_outputs(cfg, small, workloads.torch_to_host(out), delta, out_ref, np.arange(T))
+    block.close()
+
+
+@pytest.mark.parametrize("path", [STREAM, MFMA])
+def test_first_call_captured_in_a_graph(path):
+    """A forward call creates no HIP object (the side stream of the shared expert and
+    its events come from plan creation), so even a plan's first call can be captured
+    into a graph.  Each replay, with eager calls and synchronisations between them,
+    must equal an uncaptured call bit for bit."""
+    cfg = workloads.config("tiny_fp32", dtype="bf16", T=64, d=512, E=16, I=256, Is=256, k=4)
+    cfg, small, route, tin = prepare(cfg, seed=23)
+    ref_block, ref = run_gpu(cfg, tin, path)
+    block = make_block(cfg, tin, path)
+    x = tin["x"]
+    out = torch.empty_like(x)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        block.forward(x, out=out)
+    for rep in range(3):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), "replay %d differs from the eager call" % rep
+        _, again = run_gpu(cfg, tin, path, block=ref_block)  # eager work between replays
+        assert torch.equal(again, ref)
+    block.close()
+    ref_block.close()
 
 
 # ----------------------------------------------------------------------------- fused decode
