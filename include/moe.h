@@ -153,6 +153,31 @@ MOE_API moe_status_t moe_block_forward(moe_plan_t plan, void* workspace, size_t 
                                const void* shared_down, int32_t top_k, float routed_scale,
                                void* out);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): moe_block_forward with
+ * its workspace taken from a static buffer of MOE_STATIC_WORKSPACE_BYTES (128 MiB)
+ * that the library holds in each GPU's memory from its load on that GPU until
+ * the process ends; the caller passes no workspace.  The call allocates nothing
+ * (no hipMalloc, no allocating library routine); its first call on a device
+ * that no plan was created on looks the buffer's address up once.
+ *  - Arguments, layouts, errors and results as for moe_block_forward;
+ *    WORKSPACE_TOO_SMALL when the plan's workspace_bytes exceeds
+ *    MOE_STATIC_WORKSPACE_BYTES (the GLM-5 decode plan for 64 tokens needs
+ *    about 122 MiB and fits; prefill-sized plans do not).
+ *  - Every call on one GPU, from any plan or thread, shares that GPU's buffer,
+ *    which keeps the last call's contents (the kernels need nothing zeroed):
+ *    calls that overlap in time on one GPU (on different streams, or from
+ *    several host threads without ordering) race and give wrong results.  Order
+ *    them on one stream. */
+#define MOE_STATIC_WORKSPACE_BYTES ((size_t)128 << 20)
+MOE_API moe_status_t moe_block_forward_static(moe_plan_t plan, void* stream, int64_t num_tokens,
+                                              const void* x, const void* norm_w,
+                                              const void* router_w, const float* corr_bias,
+                                              const void* gate_up, const void* down,
+                                              const void* shared_gate, const void* shared_up,
+                                              const void* shared_down, int32_t top_k,
+                                              float routed_scale, void* out);
+
 /* Dense block: the blocks in front of the first MoE block use a dense SwiGLU MLP
  * instead of the MoE ("GLM-5 · Input features", excerpt block: the first
  * first_k_dense_replace blocks; excerpt mlp: GlmMoeDsaMLP, down(silu(gate x) *

@@ -319,6 +319,38 @@ SideStream* side_stream(moe_plan* p) {
 
 }  // namespace
 
+// Workspace of moe_block_forward_static: one static buffer in every GPU's memory,
+// held from the library's load on that GPU until the process ends.  In host code
+// `scratch` only names a host-side stand-in; kernels get the device address that
+// hipGetSymbolAddress returns for the current device (static_workspace below).
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_WORKSPACE_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxSideDevices];  // device address of `scratch` per device, once resolved
+
+// Device address of `scratch` on the current device, resolved once per device
+// (with that device current) and kept.
+hipError_t static_workspace(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxSideDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress((void**)&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
@@ -370,6 +402,13 @@ moe_status_t moe_plan_create(const moe_config_t* cfg, moe_plan_t* plan, size_t* 
   make_layout(p);
   // the streaming path runs the shared expert on a side stream
   if (!dense && cfg->shared_inter > 0 && cfg->path != MOE_PATH_MFMA) make_side_stream(p);
+  // set-up of moe_block_forward_static on this device, so that its calls (under graph
+  // capture, say) do no more than look the address up; without a device this fails
+  // and the entry point retries on its first call
+  if (!dense) {
+    void* unused = nullptr;
+    if (static_workspace(&unused) != hipSuccess) (void)hipGetLastError();
+  }
   *plan = p;
   *workspace_bytes = p->lay.total;
   return MOE_SUCCESS;
@@ -643,6 +682,21 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
                           k, out, s);
   });
   return err == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
+}
+
+moe_status_t moe_block_forward_static(moe_plan_t p, void* stream, int64_t T, const void* x,
+                                      const void* norm_w, const void* router_w,
+                                      const float* corr_bias, const void* gate_up,
+                                      const void* down, const void* shared_gate,
+                                      const void* shared_up, const void* shared_down, int32_t k,
+                                      float routed_scale, void* out) {
+  if (!p) return MOE_ERROR_INVALID_VALUE;
+  if (p->lay.total > MOE_STATIC_WORKSPACE_BYTES) return MOE_ERROR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (static_workspace(&ws) != hipSuccess) return MOE_ERROR_HIP;
+  return moe_block_forward(p, ws, MOE_STATIC_WORKSPACE_BYTES, stream, T, x, norm_w, router_w,
+                           corr_bias, gate_up, down, shared_gate, shared_up, shared_down, k,
+                           routed_scale, out);
 }
 
 moe_status_t moe_dense_block_forward(moe_plan_t p, void* workspace, size_t workspace_bytes,

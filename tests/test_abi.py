@@ -293,3 +293,25 @@ def test_dense_split_partials_fit_every_token_count(max_tokens):
             moe.moe_plan_check(plan, 4, 1)
     finally:
         moe.moe_plan_destroy(plan)
+
+
+def test_static_entry_point_limit():
+    """moe_block_forward_static takes the plans whose workspace fits its static buffer
+    (the GLM-5 decode plan for 64 tokens does) and rejects larger ones before any
+    device work."""
+    lib = moe.load()
+    plan, ws = moe.moe_plan_create(_cfg(max_tokens=64))
+    try:
+        assert ws <= moe.STATIC_WORKSPACE_BYTES
+    finally:
+        moe.moe_plan_destroy(plan)
+    plan, ws = moe.moe_plan_create(_cfg(max_tokens=4096))
+    try:
+        assert ws > moe.STATIC_WORKSPACE_BYTES
+        X = 0x100000
+        assert lib.moe_block_forward_static(plan, 0, 8, X, X, X, X, X, X, X, X, X, 8, 2.5, X) == \
+            moe.MOE_ERROR_WORKSPACE_TOO_SMALL
+    finally:
+        moe.moe_plan_destroy(plan)
+    assert lib.moe_block_forward_static(None, 0, 8, X, X, X, X, X, X, X, X, X, 8, 2.5, X) == \
+        moe.MOE_ERROR_INVALID_VALUE
