@@ -14,6 +14,7 @@ Output: one JSON line on stdout.  Progress goes to stderr.
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -31,9 +32,9 @@ def log(*a):
 
 
 def measured_traffic(workload, stage):
-    """HBM bytes per launch of `stage` on `workload` from profiles/traffic.txt (rocprofv3
-    FETCH_SIZE + WRITE_SIZE, scaled by a plain-copy calibration), or None when no record
-    exists or the kernel's sources changed since the counters were taken."""
+    """HBM-side bytes per launch of `stage` on `workload` from profiles/traffic.txt (rocprofv3
+    counts of the L2's read and write requests to the memory fabric, by request size), or
+    None when no record exists or the kernel's sources changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.txt")
     if not os.path.exists(path):
@@ -70,6 +71,48 @@ def algorithmic(cfg, counts):
                 gu_unit_bytes=gu_unit_bytes, gu_bytes=gu_bytes, gu_flops=gu_flops)
 
 
+ATTAINABLE = {}  # measured peaks of this GPU: "hbm" GB/s (read stream), "mfma" TFLOP/s (bf16)
+
+
+def measure_peaks(launches=10):
+    """The attainable HBM read rate and bf16 MFMA rate of this GPU, from the library's
+    measurement kernels (moe_calib_hbm_read over 4 GiB on 256 blocks of 1024 lanes;
+    moe_calib_mfma on 512 blocks of 8 waves), timed with HIP events."""
+    import torch
+    import mixture_experts_transformer_rmsnorm_amd as moe
+    nbytes = 4 << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        moe.moe_calib_hbm_read(None, buf, nbytes, 256, sink)
+    e0.record()
+    for _ in range(launches):
+        moe.moe_calib_hbm_read(None, buf, nbytes, 256, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    hbm = nbytes * launches / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    iters, blocks = 4096, 512
+    for _ in range(2):
+        moe.moe_calib_mfma(None, iters, blocks, sink)
+    e0.record()
+    flops = 0.0
+    for _ in range(launches):
+        flops += moe.moe_calib_mfma(None, iters, blocks, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    mfma = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    ATTAINABLE.update(hbm=hbm, mfma=mfma)
+    log("attainable peaks: HBM read %.1f GB/s, bf16 MFMA %.1f TFLOP/s" % (hbm, mfma))
+    return {"hbm_read_GB_per_s": round(hbm, 1), "mfma_bf16_TFLOP_per_s": round(mfma, 1),
+            "hbm_read_frac_of_published": round(hbm / HBM_PEAK_GBS, 4),
+            "mfma_frac_of_published": round(mfma / BF16_PEAK_TFLOPS, 4),
+            "how": "moe_calib_hbm_read: 4 GiB, 256 blocks x 1024 lanes, 16-byte nontemporal "
+                   "loads; moe_calib_mfma: 512 blocks x 8 waves x 4096 rounds of 4 "
+                   "independent v_mfma_f32_32x32x16_bf16; HIP events over %d launches" % launches}
+
+
 def run_workload(cfg, tin, steps, warmup):
     import torch
     import mixture_experts_transformer_rmsnorm_amd as moe
@@ -91,12 +134,16 @@ def run_workload(cfg, tin, steps, warmup):
     # timed region: K steps; HIP events on the forward's stream around the dominant kernel
     moe.moe_set_stage_timing(block.plan, moe.stage_mask(DOMINANT))
     moe.moe_stage_times(block.plan)  # reset
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    ev[0].record(stream)
+    for i in range(steps):
         block.forward(x, out=out, stream=stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     stage_ms, calls = moe.moe_stage_times(block.plan)
     moe.moe_set_stage_timing(block.plan, 0)
 
@@ -125,6 +172,10 @@ def run_workload(cfg, tin, steps, warmup):
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
     roof["traffic"] = measured_traffic(cfg.name, DOMINANT)
+    if ATTAINABLE:
+        att = ATTAINABLE["hbm"] if roof["bound"] == "hbm" else ATTAINABLE["mfma"]
+        roof["attainable"] = round(att, 1)
+        roof["frac_of_attainable"] = round(achieved / att, 4)
     roof.update(kernel=DOMINANT, kernel_ms=round(gu_ms, 4), algorithmic_bytes=alg["gu_bytes"],
                 algorithmic_flops=alg["gu_flops"], active_experts=alg["n_active"])
     if roof["traffic"]:
@@ -138,49 +189,136 @@ def run_workload(cfg, tin, steps, warmup):
                  "TFLOP_per_s": round(alg["step_flops"] / step_s / 1e12, 1),
                  "hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
                  "frac": round(t_roof / step_s, 4)}
+    if ATTAINABLE:
+        t_att = max(alg["step_bytes"] / (ATTAINABLE["hbm"] * 1e9),
+                    alg["step_flops"] / (ATTAINABLE["mfma"] * 1e12))
+        step_roof["frac_of_attainable"] = round(t_att / step_s, 4)
     per_stage = {k: round(v / max(all_calls, 1), 4) for k, v in all_ms.items() if v > 0}
-    return dict(value=cfg.T * steps / elapsed, ms_per_step=ms_step, roofline=roof,
+    return dict(value=cfg.T * steps / elapsed, ms_per_step=ms_step,
+                ms_per_step_median=step_ms[len(step_ms) // 2], ms_per_step_min=step_ms[0],
+                roofline=roof,
                 step_roofline=step_roof, stage_ms=per_stage, path=path,
                 max_load=int(counts.max()), counts=counts)
 
 
-def cpu_baseline(cfg, tin, small, seconds):
-    """The CPU oracle, as it stands, on the first tokens of the same batch, in chunks
-    of 8 tokens until about `seconds` of oracle time (full forward: norm, router,
-    selected experts, shared expert, combine)."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+class _HostExperts:
+    """Host copies (bf16 bits) of the device expert weights the oracle needs."""
+
+    def __init__(self, cfg, tin):
+        import workloads
+        self.cfg, self.tin = cfg, tin
+        self.gu, self.dn = {}, {}
+        self.shared = ([workloads.torch_to_host(tin[n]) for n in ("shared_gate", "shared_up",
+                                                                  "shared_down")]
+                       if cfg.Is else [None, None, None])
+
+    def lists(self, experts):
+        import workloads
+        for e in experts:
+            if e not in self.gu:
+                self.gu[e] = workloads.torch_to_host(self.tin["gate_up"][e])
+                self.dn[e] = workloads.torch_to_host(self.tin["down"][e])
+        return ([self.gu.get(e) for e in range(self.cfg.E)],
+                [self.dn.get(e) for e in range(self.cfg.E)])
+
+
+def _oracle_seconds(cfg, small, hosts, rows):
+    """Oracle time of the full forward (norm, router, selection, the selected experts and
+    the shared expert, combine) on the given rows of the batch; weight copies to the host
+    happen before the clock starts."""
     import numpy as np
+    import oracle
+    dt = oracle.DTYPES[cfg.dtype]
+    xs = small["x"][rows]
+    pre = oracle.route(xs, small["norm_w"], small["router_w"], small["corr_bias"], cfg.k,
+                       cfg.routed_scale, dt, cfg.eps)
+    gu, dn = hosts.lists(np.unique(pre["idx"]))
+    sh = hosts.shared
+    t0 = time.perf_counter()
+    r = oracle.route(xs, small["norm_w"], small["router_w"], small["corr_bias"], cfg.k,
+                     cfg.routed_scale, dt, cfg.eps)
+    oracle.experts(np.arange(len(rows)), xs, r["h"], r["idx"], r["w"], gu, dn, sh[0], sh[1],
+                   sh[2], dt)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(cfg, tin, small, seconds):
+    """The CPU oracle, as it stands, timed on this machine's host cores.
+
+    Headline: the first tokens of the same decode batch, in chunks of 8 tokens until
+    about `seconds` of oracle time, on the oracle's OpenMP threads (the process's CPU
+    share).  Beside it: single-thread rates on the tiny fp32 workload (whole batch)
+    and on 4 decode tokens; and per-token rates on 16 tokens of the 4096-token prefill
+    and of the mid-size workload, extrapolated to their whole batches."""
+    import numpy as np
+    import torch
     import oracle
     import workloads
 
-    dt = oracle.DTYPES[cfg.dtype]
-    host_gu, host_dn = {}, {}
-    shared = [workloads.torch_to_host(tin[n]) for n in ("shared_gate", "shared_up", "shared_down")]
-    spent, done = 0.0, 0
-    chunk = 8
+    threads = oracle.num_threads()
+    hosts = _HostExperts(cfg, tin)
+    spent, done, chunk = 0.0, 0, 8
     while done < cfg.T and (spent < seconds or done == 0):
         rows = np.arange(done, min(cfg.T, done + chunk))
-        xs = small["x"][rows]
-        # routing of the chunk decides which expert weights the oracle needs on the host
-        pre = oracle.route(xs, small["norm_w"], small["router_w"], small["corr_bias"], cfg.k,
-                           cfg.routed_scale, dt, cfg.eps)
-        for e in np.unique(pre["idx"]):
-            if e not in host_gu:
-                host_gu[e] = workloads.torch_to_host(tin["gate_up"][e])
-                host_dn[e] = workloads.torch_to_host(tin["down"][e])
-        gu = [host_gu.get(e) for e in range(cfg.E)]
-        dn = [host_dn.get(e) for e in range(cfg.E)]
-        t0 = time.perf_counter()
-        r = oracle.route(xs, small["norm_w"], small["router_w"], small["corr_bias"], cfg.k,
-                         cfg.routed_scale, dt, cfg.eps)
-        oracle.experts(np.arange(len(rows)), xs, r["h"], r["idx"], r["w"], gu, dn, shared[0],
-                       shared[1], shared[2], dt)
-        spent += time.perf_counter() - t0
+        spent += _oracle_seconds(cfg, small, hosts, rows)
         done += len(rows)
         log("cpu oracle: %d tokens in %.1f s" % (done, spent))
-    return {"value": round(done / spent, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": "first %d of the %d %s tokens, full forward (norm, router, %d experts "
-                      "+ shared, combine), %.1f s" % (done, cfg.T, cfg.name, cfg.k, spent)}
+    res = {"value": round(done / spent, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": "first %d of the %d %s tokens, full forward (norm, router, %d experts "
+                     "+ shared, combine), %.1f s on %d OpenMP threads" % (
+                         done, cfg.T, cfg.name, cfg.k, spent, threads),
+           "cpu_model": cpu_model(), "cores_available": len(os.sched_getaffinity(0))}
+
+    # single thread: the tiny fp32 workload in full, and 4 decode tokens
+    single = {}
+    tiny = workloads.config("tiny_fp32")
+    host = workloads.make_host(tiny, 0)
+    for n in (1, threads):
+        oracle.set_num_threads(n)
+        t0 = time.perf_counter()
+        oracle.forward(host)
+        dt_s = time.perf_counter() - t0
+        single["tiny_fp32_%dthread%s" % (n, "" if n == 1 else "s")] = {
+            "tokens": tiny.T, "seconds": round(dt_s, 4), "tokens_per_s": round(tiny.T / dt_s, 1)}
+    oracle.set_num_threads(1)
+    t1 = _oracle_seconds(cfg, small, hosts, np.arange(4))
+    oracle.set_num_threads(threads)
+    single["%s_1thread" % cfg.name] = {"tokens": 4, "seconds": round(t1, 3),
+                                       "tokens_per_s": round(4 / t1, 3)}
+    log("cpu oracle, 1 thread: %s 4 tokens in %.2f s" % (cfg.name, t1))
+    res["single_thread"] = single
+
+    # per-token time on 16 tokens of the prefill workloads, times their batch size
+    extra = {}
+    for name in ("glm5_prefill", "mid_prefill"):
+        c2 = workloads.config(name)
+        s2 = workloads.draw_small(c2, 0)
+        same = (c2.d, c2.E, c2.I, c2.Is, c2.dtype) == (cfg.d, cfg.E, cfg.I, cfg.Is, cfg.dtype)
+        t2 = tin if same else workloads.make_torch(c2, 0, device="cuda", weights="device")
+        h2 = hosts if same else _HostExperts(c2, t2)
+        n = 16
+        sec = _oracle_seconds(c2, s2, h2, np.arange(n))
+        extra[name] = {"tokens_timed": n, "seconds": round(sec, 3), "tokens_per_s": round(n / sec, 3),
+                       "batch_tokens": c2.T, "batch_seconds_extrapolated": round(sec / n * c2.T, 1),
+                       "threads": threads}
+        log("cpu oracle: %s %d tokens in %.2f s (batch of %d: %.0f s extrapolated)" % (
+            name, n, sec, c2.T, sec / n * c2.T))
+        if not same:
+            del h2, t2
+            torch.cuda.empty_cache()
+    res["extrapolated"] = extra
+    return res
 
 
 def measure_norms(launches):
@@ -371,6 +509,8 @@ def main():
                     help="second workload of the same shape family reported in the line ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring the attainable HBM-read and MFMA rates")
     ap.add_argument("--extras", default="norms,dense,pack,sweep,configs",
                     help="comma list of extra measurements put into the line's 'extras' "
                          "('norms', 'dense', 'pack', 'sweep': the block at other batch "
@@ -401,6 +541,7 @@ def main():
         log("calibration copy: %d bytes read, %d bytes written" % (n, n))
         del src, dst
     extras_req = [e for e in args.extras.split(",") if e]
+    peaks = None if args.no_peaks else measure_peaks()
 
     def run_extras(cfg=None, tin=None):
         ext = {}
@@ -432,6 +573,8 @@ def main():
     line = {
         "metric": METRIC, "value": round(res["value"], 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4),
+        "ms_per_step_median": round(res["ms_per_step_median"], 4),
+        "ms_per_step_min": round(res["ms_per_step_min"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
         "data": "synthetic (seeded; random-init weights of the GLM-5 MoE-block shapes)",
         "config": {"workload": cfg.name, "tokens": cfg.T, "dim": cfg.d, "n_experts": cfg.E,
@@ -443,6 +586,8 @@ def main():
         "step_roofline": res["step_roofline"],
         "stage_ms": res["stage_ms"],
     }
+    if peaks:
+        line["attainable"] = peaks
     if args.secondary:
         cfg2 = workloads.config(args.secondary)
         if (cfg2.d, cfg2.E, cfg2.I, cfg2.Is, cfg2.dtype) == (cfg.d, cfg.E, cfg.I, cfg.Is, cfg.dtype):
@@ -459,6 +604,8 @@ def main():
             line["secondary"] = {"workload": cfg2.name, "tokens": cfg2.T,
                                  "value": round(r2["value"], 1), "unit": "tokens/s",
                                  "ms_per_step": round(r2["ms_per_step"], 4),
+                                 "ms_per_step_median": round(r2["ms_per_step_median"], 4),
+                                 "ms_per_step_min": round(r2["ms_per_step_min"], 4),
                                  "kernel_path": "stream" if r2["path"] == 1 else "mfma",
                                  "roofline": r2["roofline"], "step_roofline": r2["step_roofline"],
                                  "stage_ms": r2["stage_ms"]}

@@ -97,8 +97,12 @@ typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
  *          HBM), MFMA otherwise.  fp32 plans always use STREAM.
  *  STREAM: weight-streaming FMA kernels (any dtype).
  *  MFMA:   LDS-tiled bf16 matrix-core kernels (bf16 only).
- *  FUSED:  reserved for a single persistent decode kernel; not available in this
- *          build (moe_plan_create returns NOT_SUPPORTED). */
+ *  FUSED:  the whole forward in one launch (bf16 only) for calls of at most 64
+ *          tokens: one block per compute unit, all resident at once (cooperative
+ *          launch), the steps separated by grid barriers; larger calls of a FUSED
+ *          plan take the STREAM kernels.  Forward returns NOT_SUPPORTED on a device
+ *          without cooperative launch.  AUTO does not pick it (slower than the
+ *          multi-kernel path at the batch sizes measured). */
 typedef enum {
   MOE_PATH_AUTO = 0,
   MOE_PATH_STREAM = 1,
@@ -263,6 +267,22 @@ MOE_API moe_status_t moe_rmsnorm(void* stream, int32_t dtype, int64_t rows, int3
                                  const void* x, int64_t x_stride, const void* weight, void* out,
                                  int64_t out_stride);
 
+/* Measurement kernels: the attainable peaks of this GPU, for reporting the
+ * sublayer's kernels against them beside the published peaks.
+ *  moe_calib_hbm_read: reads `bytes` (a multiple of 16) of device buffer src
+ *    (16-byte aligned), each of `blocks` blocks of 1024 lanes an equal contiguous
+ *    share, with 16-byte nontemporal loads.  sink: 4 bytes of device memory,
+ *    written only for a data pattern that real buffers do not produce.
+ *  moe_calib_mfma: `blocks` blocks of 8 waves, each wave `iters` rounds of four
+ *    independent v_mfma_f32_32x32x16_bf16 on register operands; *flops (host)
+ *    receives the FLOPs enqueued; sink as above.
+ * Both enqueue on `stream` and return asynchronously; the caller times them
+ * (events around the call).  INVALID_VALUE / MISALIGNED for bad arguments. */
+MOE_API moe_status_t moe_calib_hbm_read(void* stream, const void* src, size_t bytes, int32_t blocks,
+                                        void* sink);
+MOE_API moe_status_t moe_calib_mfma(void* stream, int32_t iters, int32_t blocks, void* sink,
+                                    double* flops);
+
 /* Intermediate buffers of the last forward call (tests, diagnostics). */
 typedef enum {
   MOE_BUF_H = 0,          /* [T, d] D: normalised input */
@@ -272,8 +292,9 @@ typedef enum {
   MOE_BUF_ACT = 4,        /* [T*k, I] D: silu(gate) * up per permuted row */
   MOE_BUF_Y = 5,          /* [T*k, d] D: routed expert output per permuted row */
   MOE_BUF_SHARED_ACT = 6, /* [T, Is] D: shared expert silu(gate) * up */
-  MOE_BUF_FUSED_ERROR = 7, /* [1] uint32: error word of the fused decode kernel (reserved;
-                              0 while that kernel is not available) */
+  MOE_BUF_FUSED_ERROR = 7, /* [1] uint32: error word of the last fused decode launch: 0, or
+                              nonzero if a grid-barrier wait ran out of time (1 s) and the
+                              launch ended early (outputs then undefined) */
   MOE_BUF_COUNT = 8
 } moe_buffer_t;
 

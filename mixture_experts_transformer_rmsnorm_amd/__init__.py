@@ -37,7 +37,8 @@ EXPORTS = ("moe_plan_create", "moe_plan_destroy", "moe_block_forward", "moe_read
            "moe_read_buffer", "moe_buffer_bytes", "moe_plan_path", "moe_set_stage_timing",
            "moe_stage_times", "moe_stage_name", "moe_status_string", "moe_abi_version",
            "moe_rmsnorm", "moe_dense_block_forward", "moe_pack_expert", "moe_unpack_expert",
-           "moe_plan_check", "moe_block_forward_static")
+           "moe_plan_check", "moe_block_forward_static", "moe_calib_hbm_read",
+           "moe_calib_mfma")
 STATIC_WORKSPACE_BYTES = 128 << 20
 
 
@@ -81,6 +82,8 @@ def load(path: str = LIB_PATH):
                                           i32, ctypes.c_float, P]
         lib.moe_block_forward_static.argtypes = [P, P, i64, P, P, P, P, P, P, P, P, P, i32,
                                                  ctypes.c_float, P]
+        lib.moe_calib_hbm_read.argtypes = [P, P, ctypes.c_size_t, i32, P]
+        lib.moe_calib_mfma.argtypes = [P, i32, i32, P, ctypes.POINTER(ctypes.c_double)]
         lib.moe_read_routing.argtypes = [P, P, P, i64, i32, P, P, P]
         lib.moe_read_buffer.argtypes = [P, P, P, i64, i32, i32, P, ctypes.c_size_t]
         lib.moe_buffer_bytes.argtypes = [P, i64, i32, i32]
@@ -103,7 +106,8 @@ def load(path: str = LIB_PATH):
         for fn in ("moe_plan_create", "moe_plan_destroy", "moe_block_forward", "moe_read_routing",
                    "moe_read_buffer", "moe_set_stage_timing", "moe_stage_times", "moe_rmsnorm",
                    "moe_dense_block_forward", "moe_pack_expert", "moe_unpack_expert",
-                   "moe_plan_check", "moe_block_forward_static"):
+                   "moe_plan_check", "moe_block_forward_static", "moe_calib_hbm_read",
+           "moe_calib_mfma"):
             getattr(lib, fn).restype = i32
         if lib.moe_abi_version() != ABI_VERSION:
             raise ImportError("libmoe_mi355x.so ABI %d != binding ABI %d"
@@ -187,6 +191,19 @@ def moe_block_forward_static(plan, stream, num_tokens, x, norm_w, router_w, corr
         plan, _stream(stream), num_tokens, _ptr(x), _ptr(norm_w), _ptr(router_w), _ptr(corr_bias),
         _ptr(gate_up), _ptr(down), _ptr(shared_gate), _ptr(shared_up), _ptr(shared_down), top_k,
         routed_scale, _ptr(out)), "moe_block_forward_static")
+
+
+def moe_calib_hbm_read(stream, src, nbytes, blocks, sink) -> None:
+    _check(load().moe_calib_hbm_read(_stream(stream), _ptr(src), nbytes, blocks, _ptr(sink)),
+           "moe_calib_hbm_read")
+
+
+def moe_calib_mfma(stream, iters, blocks, sink) -> float:
+    """Enqueues the MFMA loop; returns the FLOPs it performs."""
+    flops = ctypes.c_double()
+    _check(load().moe_calib_mfma(_stream(stream), iters, blocks, _ptr(sink), ctypes.byref(flops)),
+           "moe_calib_mfma")
+    return flops.value
 
 
 def moe_rmsnorm(stream, dtype, rows, width, eps, x, x_stride, weight, out, out_stride) -> None:

@@ -351,6 +351,7 @@ __global__ __launch_bounds__(NB_THREADS) void mfma_nt_big_kernel(MfmaProblem p) 
 // is unrolled over both rings (6 steps), so that the compiler sees that the
 // reads of step t do not depend on the loads just issued into other slots.
 constexpr int GB_M = kGroupBM, GB_N = 256, GB_K = 64, GB_THREADS = 512;
+constexpr int kGroupMT = 4;  // M-tiles of one expert per group of the tile order
 constexpr int GB_A_ELEMS = GB_M * GB_K, GB_B_ELEMS = GB_K * GB_N;  // 32 KiB each
 constexpr int GB_ACT_COLS = GB_N / 2;
 constexpr int GB_A_LOADS = GB_A_ELEMS / (GB_THREADS * 8);  // per thread and step: 4
@@ -365,7 +366,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // outstanding and all of its LDS operations have completed.
 constexpr int waitcnt_vm_lgkm0(int n) { return 0x0070 | n; }
 
-template <int EPI>
+template <int EPI, int BAUX>
 __global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p) {
   __shared__ __attribute__((aligned(1024))) uint16_t sa0[GB_A_ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t sa1[GB_A_ELEMS];
@@ -387,9 +388,22 @@ __global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p)
   if (slot >= per) return;
   const int logical = (blockIdx.x % kXcds) * per + slot;
   if (logical >= total) return;
-  const int2 tt = p.mtiles[logical / n_tiles];
-  const int n_tile = logical % n_tiles;
-  const int e = tt.x, m0 = tt.y, seg = p.offsets[e];
+  // The tiles of one expert hold the logical range [b * n_tiles, (b + me) * n_tiles)
+  // (its M-tiles are entries b .. b + me - 1 of the M-tile list).  Inside that range
+  // they go in groups of kGroupMT M-tiles, N-tile outer and M-tile inner, so that
+  // the blocks that read the same weight columns are adjacent (they start together
+  // on one XCD and share its L2), and the 32 blocks an XCD runs at a time cover about
+  // 4 M-tiles x 8 N-tiles of a busy expert instead of 2 x 16.
+  const int q = logical / n_tiles;
+  const int e = p.mtiles[q].x;
+  const int b = q - p.mtiles[q].y / GB_M;
+  const int me = (p.counts[e] + GB_M - 1) / GB_M;
+  const int j = logical - b * n_tiles;
+  const int g0 = j / (kGroupMT * n_tiles) * kGroupMT;
+  const int gsz = min(kGroupMT, me - g0);
+  const int jj = j - g0 * n_tiles;
+  const int n_tile = jj / gsz;
+  const int m0 = (g0 + jj % gsz) * GB_M, seg = p.offsets[e];
   const int rows = min(GB_M, p.counts[e] - m0);
   const int nkt = p.K / GB_K;
 
@@ -429,10 +443,13 @@ __global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p)
     b_src[i] = p.Bg + (int64_t)e * p.b_stride + (int64_t)k * p.ldb + gcol;
   }
   const int64_t b_kstep = (int64_t)GB_K * p.ldb;
-  // Weight loads of gate_up are marked nontemporal (cache-policy bit 1 of the
-  // instruction), which keeps the gathered activation rows in L2 (gate_up 4 %
-  // faster); for down, whose activation tile is small, the plain policy is faster.
-  constexpr int kBAux = EPI == kEpiSwiGLU ? 2 : 0;
+  // Weight loads with cache-policy bits BAUX: nontemporal (2) for gate_up when the
+  // experts average fewer rows than one M-tile, so that no other block reads the
+  // same weights and keeping them out of L2 keeps the gathered activation rows
+  // there (4096-token GLM-5 prefill: gate_up 6 % faster); plain (0) when experts
+  // span several M-tiles, whose blocks read each weight column at about the same
+  // time on the same XCD through L2 (mid-size and Zipf prefill: 2-5 % faster), and
+  // for down, whose activation tile is small.
   auto issue_a = [&](uint16_t* dst, int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < GB_A_LOADS; ++i)
@@ -444,7 +461,7 @@ __global__ __launch_bounds__(GB_THREADS) void mfma_grouped_kernel(MfmaProblem p)
 #pragma unroll
     for (int i = 0; i < GB_B_LOADS; ++i)
       __builtin_amdgcn_global_load_lds(b_src[i] + kt * b_kstep,
-                                       (lds_void_t*)(dst + (4 * w + i) * 512), 16, 0, kBAux);
+                                       (lds_void_t*)(dst + (4 * w + i) * 512), 16, 0, BAUX);
   };
 
   // ---- compute side
@@ -831,7 +848,7 @@ hipError_t launch_mfma_nt_swiglu(const NtArgs& a, void* act, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_mfma_gate_up(const GroupArgs& g, int max_mtiles, const void* h,
+hipError_t launch_mfma_gate_up(const GroupArgs& g, int max_mtiles, int64_t rows, const void* h,
                                const void* gate_up, void* act, hipStream_t s) {
   if (max_mtiles == 0) return hipSuccess;
   MfmaProblem p = {};
@@ -852,7 +869,10 @@ hipError_t launch_mfma_gate_up(const GroupArgs& g, int max_mtiles, const void* h
   p.ldc = g.I;
   p.n_tiles = (g.I + GB_ACT_COLS - 1) / GB_ACT_COLS;
   const int64_t blocks = ((int64_t)p.n_tiles * max_mtiles + kXcds - 1) / kXcds * kXcds;
-  mfma_grouped_kernel<kEpiSwiGLU><<<dim3((unsigned)blocks), GB_THREADS, 0, s>>>(p);
+  if (rows < (int64_t)GB_M * g.E)  // fewer rows than one M-tile per expert on average
+    mfma_grouped_kernel<kEpiSwiGLU, 2><<<dim3((unsigned)blocks), GB_THREADS, 0, s>>>(p);
+  else
+    mfma_grouped_kernel<kEpiSwiGLU, 0><<<dim3((unsigned)blocks), GB_THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -876,7 +896,7 @@ hipError_t launch_mfma_down(const GroupArgs& g, int max_mtiles, const void* act,
   p.ldc = g.d;
   p.n_tiles = (g.d + GB_N - 1) / GB_N;
   const int64_t blocks = ((int64_t)p.n_tiles * max_mtiles + kXcds - 1) / kXcds * kXcds;
-  mfma_grouped_kernel<kEpiStore><<<dim3((unsigned)blocks), GB_THREADS, 0, s>>>(p);
+  mfma_grouped_kernel<kEpiStore, 0><<<dim3((unsigned)blocks), GB_THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 

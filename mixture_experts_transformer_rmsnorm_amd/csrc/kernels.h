@@ -163,21 +163,24 @@ hipError_t launch_stream_gate_up(int dtype, const GroupArgs& g, const StreamFix&
 hipError_t launch_stream_down(int dtype, const GroupArgs& g, const StreamFix& fx,
                               const void* act, const void* down, void* y, hipStream_t s);
 
-hipError_t launch_mfma_gate_up(const GroupArgs& g, int max_mtiles, const void* h,
+// rows: T * k, the permuted rows of the call (it picks the weight loads' cache policy)
+hipError_t launch_mfma_gate_up(const GroupArgs& g, int max_mtiles, int64_t rows, const void* h,
                                const void* gate_up, void* act, hipStream_t s);
 hipError_t launch_mfma_down(const GroupArgs& g, int max_mtiles, const void* act, const void* down,
                             void* y, hipStream_t s);
 
+// ---------------------------------------------------------------- measurement
+// Reads bytes (a multiple of 16) of src on `blocks` blocks; sink [1] is written only
+// in a case that never arises for real data (it keeps the loads).
+hipError_t launch_calib_read(const void* src, size_t bytes, int blocks, uint32_t* sink,
+                             hipStream_t s);
+// `iters` rounds of MFMAs on `blocks` blocks; *flops receives the FLOPs enqueued.
+hipError_t launch_calib_mfma(int iters, int blocks, float* sink, double* flops, hipStream_t s);
+
 // ---------------------------------------------------------------- fused decode
-// Phases of the fused decode kernel, in the order its items are handed out; every
-// phase depends only on earlier ones.
-enum FusedPhase {
-  kPhNorm = 0, kPhRouter, kPhTopk, kPhScan, kPhScatter, kPhShGu, kPhGu, kPhShAct, kPhShDn, kPhDn,
-  kPhCombine, kFusedPhases
-};
-// Words of the fused kernel's synchronisation state: ticket, error flag, one done
-// counter per phase, one per expert (its gate/up items).
-inline int kFusedSyncWords(int E) { return 2 + kFusedPhases + E; }
+// Words of the fused kernel's synchronisation state: grid-barrier arrivals,
+// barrier generation, error flag (set when a barrier wait ran out of time).
+constexpr int kFusedSyncWords = 4;
 
 struct bf16;
 struct FusedArgs {
@@ -204,6 +207,7 @@ struct FusedArgs {
   int32_t* offsets;
   RouteHeader* hdr;
   int32_t* active;
+  int32_t* pass_base;
   int32_t* perm_token;
   int32_t* row_of;
   bf16* act;
@@ -211,14 +215,17 @@ struct FusedArgs {
   float* sh_gu;
   bf16* act_s;
   float* sh_dn;
+  float* parts;  // partial sums of the weight streams' split items
   // split-K of the router and shared-expert products
   int r_splits, r_kper, sg_splits, sg_kper, sd_splits, sd_kper;
-  uint32_t* sync;                // kFusedSyncWords(E) words
-  int start[kFusedPhases + 1];   // first item of each phase (set by the launcher)
+  uint32_t* sync;  // kFusedSyncWords words
 };
-// Items of each phase; returns the total.
-int fused_item_counts(const FusedArgs& f, int* counts);
-// Resets the synchronisation state, then runs the persistent kernel on `grid` blocks.
-hipError_t launch_fused_decode(FusedArgs f, int grid, hipStream_t s);
+// Blocks of the fused kernel: one per compute unit (all resident at once, by the
+// cooperative launch), at most kStreamMaxBlocks.
+hipError_t fused_decode_blocks(int* blocks);
+// Resets the synchronisation state, then runs the kernel on `blocks` blocks (a
+// cooperative launch: it fails rather than start with blocks that cannot all be
+// resident).
+hipError_t launch_fused_decode(const FusedArgs& f, int blocks, hipStream_t s);
 
 }  // namespace moe

@@ -141,22 +141,19 @@ namespace {
 
 bool use_mfma(const moe_plan* p, int64_t T, int k) {
   if (p->cfg.dtype != MOE_DTYPE_BF16) return false;
-  if (p->cfg.path == MOE_PATH_STREAM) return false;
+  if (p->cfg.path == MOE_PATH_STREAM || p->cfg.path == MOE_PATH_FUSED) return false;
   if (p->cfg.path == MOE_PATH_MFMA) return true;
   return T * k > (int64_t)kStreamMaxMeanTokens * p->cfg.n_experts;
 }
 
-// The fused decode kernel: bf16 MoE plans, at most kFusedMaxTokens tokens, under
-// MOE_PATH_FUSED or (AUTO) whenever the streaming kernels would be chosen.
-// The fused decode kernel is switched off: its first run on the GPU did not finish
-// and the cause has not been established, so no plan reaches it (plan creation
-// rejects MOE_PATH_FUSED and AUTO never picks it).
-constexpr bool kFusedEnabled = false;
+// The fused decode kernel: bf16 MoE plans under MOE_PATH_FUSED, for calls of at
+// most kFusedMaxTokens tokens (larger calls of such a plan take the streaming
+// kernels).  AUTO does not pick it: its grid barriers cost more than the launch
+// gaps of the multi-kernel path at every decode batch size measured.
 bool use_fused(const moe_plan* p, int64_t T, int k) {
-  if (!kFusedEnabled) return false;
-  if (p->cfg.dtype != MOE_DTYPE_BF16 || p->cfg.n_experts == 0 || T > kFusedMaxTokens) return false;
-  if (p->cfg.path == MOE_PATH_FUSED) return true;
-  return p->cfg.path == MOE_PATH_AUTO && !use_mfma(p, T, k);
+  (void)k;
+  return p->cfg.path == MOE_PATH_FUSED && p->cfg.dtype == MOE_DTYPE_BF16 &&
+         p->cfg.n_experts > 0 && T <= kFusedMaxTokens;
 }
 
 // Tile sizes of the dense K-contiguous products of T rows for this plan's dtype.
@@ -235,7 +232,7 @@ void make_layout(moe_plan* p) {
     L.sh_gu = L.act_s = L.sh_dn = 0;
     L.sh_gu_bytes = L.sh_dn_bytes = 0;
   }
-  L.sync = take((size_t)kFusedSyncWords(std::max(c.n_experts, 1)) * 4);
+  L.sync = take((size_t)kFusedSyncWords * 4);
   L.total = off;
 }
 
@@ -388,7 +385,6 @@ moe_status_t moe_plan_create(const moe_config_t* cfg, moe_plan_t* plan, size_t* 
   if (cfg->path < MOE_PATH_AUTO || cfg->path > MOE_PATH_FUSED) return MOE_ERROR_INVALID_VALUE;
   if ((cfg->path == MOE_PATH_MFMA || cfg->path == MOE_PATH_FUSED) && cfg->dtype != MOE_DTYPE_BF16)
     return MOE_ERROR_NOT_SUPPORTED;
-  if (cfg->path == MOE_PATH_FUSED && !kFusedEnabled) return MOE_ERROR_NOT_SUPPORTED;
   if (cfg->dim % 64 || cfg->moe_inter % 64 || cfg->shared_inter % 64 ||
       cfg->n_experts > kMaxExperts || cfg->max_top_k > kMaxTopK)
     return MOE_ERROR_NOT_SUPPORTED;
@@ -585,16 +581,18 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
     f.h = (bf16*)h, f.logits = logits, f.topk_idx = topk_idx, f.topk_w = topk_w;
     f.chunk_cnt = chunk_cnt, f.counts = counts, f.offsets = offsets, f.hdr = hdr, f.active = active;
     f.perm_token = perm_token, f.row_of = row_of, f.act = (bf16*)act, f.y = (bf16*)y;
+    f.pass_base = pass_base, f.parts = s_parts;
     f.sh_gu = sh_gu, f.act_s = (bf16*)act_s, f.sh_dn = sh_dn;
     f.r_splits = rsplit.splits, f.r_kper = rsplit.kt_per;
     f.sg_splits = sgsplit.splits, f.sg_kper = sgsplit.kt_per;
     f.sd_splits = sdsplit.splits, f.sd_kper = sdsplit.kt_per;
     f.sync = (uint32_t*)(ws + L.sync);
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return MOE_ERROR_HIP;
-    stage(kStFused, [&] { return launch_fused_decode(f, 2 * std::max(cus, 1), s); });
+    int blocks = 0;
+    if (fused_decode_blocks(&blocks) != hipSuccess) {
+      (void)hipGetLastError();
+      return MOE_ERROR_NOT_SUPPORTED;  // no cooperative launch on this device
+    }
+    stage(kStFused, [&] { return launch_fused_decode(f, blocks, s); });
     return err == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
   }
   stage(kStNorm, [&] { return launch_rmsnorm(dt, x, d, norm_w, h, d, T, d, c.eps, s); });
@@ -663,7 +661,7 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   const StreamFix fx{s_parts, stream_slot_floats(dt, I, d), 0};
   const int max_mtiles = (int)(cdiv(A, kGroupBM) + std::min<int64_t>(E, A));
   stage(kStGateUp, [&] {
-    return mfma ? launch_mfma_gate_up(g, max_mtiles, h, gate_up, act, s)
+    return mfma ? launch_mfma_gate_up(g, max_mtiles, A, h, gate_up, act, s)
                 : launch_stream_gate_up(dt, g, fx, h, gate_up, act, s);
   });
   stage(kStDown, [&] {
@@ -905,6 +903,23 @@ moe_status_t moe_rmsnorm(void* stream, int32_t dtype, int64_t rows, int32_t widt
   return e == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
 }
 
+moe_status_t moe_calib_hbm_read(void* stream, const void* src, size_t bytes, int32_t blocks,
+                                void* sink) {
+  if (!src || !sink || bytes == 0 || bytes % 16 || blocks < 1 || blocks > 65536)
+    return MOE_ERROR_INVALID_VALUE;
+  if (misaligned(src) || ((uintptr_t)sink & 3u)) return MOE_ERROR_MISALIGNED;
+  const hipError_t e = launch_calib_read(src, bytes, blocks, (uint32_t*)sink, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
+}
+
+moe_status_t moe_calib_mfma(void* stream, int32_t iters, int32_t blocks, void* sink,
+                            double* flops) {
+  if (!sink || !flops || iters < 1 || blocks < 1 || blocks > 65536) return MOE_ERROR_INVALID_VALUE;
+  if ((uintptr_t)sink & 3u) return MOE_ERROR_MISALIGNED;
+  const hipError_t e = launch_calib_mfma(iters, blocks, (float*)sink, flops, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
+}
+
 moe_status_t moe_read_buffer(moe_plan_t p, const void* workspace, void* stream, int64_t T,
                              int32_t k, int32_t which, void* dst, size_t dst_bytes) {
   if (!p || !workspace || !dst) return MOE_ERROR_INVALID_VALUE;
@@ -928,7 +943,7 @@ moe_status_t moe_read_buffer(moe_plan_t p, const void* workspace, void* stream, 
     case MOE_BUF_ACT: off = L.act; break;
     case MOE_BUF_Y: off = L.y; break;
     case MOE_BUF_SHARED_ACT: off = L.act_s; break;
-    case MOE_BUF_FUSED_ERROR: off = L.sync + 4; break;
+    case MOE_BUF_FUSED_ERROR: off = L.sync + 8; break;
   }
   const hipError_t e = hipMemcpyAsync(dst, (const char*)workspace + off, bytes,
                                       hipMemcpyDeviceToDevice, (hipStream_t)stream);

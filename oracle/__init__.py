@@ -60,7 +60,8 @@ def _load():
                                            P, P, P, P, P, P, P, P, P]
             lib.oracle_dense_mlp.argtypes = [i64, i32, i32, i32, P, P, P, P, P, P, P, P]
             lib.oracle_num_threads.argtypes = []
-            for fn in ("oracle_num_threads", "oracle_round_to_dtype", "oracle_rmsnorm", "oracle_router_scores",
+            lib.oracle_set_num_threads.argtypes = [i32]
+            for fn in ("oracle_num_threads", "oracle_set_num_threads", "oracle_round_to_dtype", "oracle_rmsnorm", "oracle_router_scores",
                        "oracle_select", "oracle_counts", "oracle_experts", "oracle_dense_mlp"):
                 getattr(lib, fn).restype = ctypes.c_int
             _lib = lib
@@ -89,6 +90,11 @@ def _check(rc, what):
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads for the oracle's next calls on this thread (timing only)."""
+    _check(_load().oracle_set_num_threads(int(n)), "set_num_threads")
 
 
 def round_to_dtype(a, dtype):

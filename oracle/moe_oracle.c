@@ -81,6 +81,13 @@ static float load_elem(const void* p, int64_t i, int dtype) {
 /* Threads an OpenMP parallel region of this library uses. */
 ORACLE_API int oracle_num_threads(void) { return omp_get_max_threads(); }
 
+/* Threads of the parallel loops that follow on the calling thread (timing only). */
+ORACLE_API int oracle_set_num_threads(int32_t n) {
+  if (n < 1) return -1;
+  omp_set_num_threads(n);
+  return 0;
+}
+
 ORACLE_API int oracle_round_to_dtype(int64_t n, const float* in, float* out, int dtype) {
   if (n < 0 || (n > 0 && (!in || !out))) return -1;
   for (int64_t i = 0; i < n; ++i) out[i] = round_to_dtype(in[i], dtype);

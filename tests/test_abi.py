@@ -54,7 +54,6 @@ def _cfg(**kw):
     (dict(dtype="f32", path=moe.MOE_PATH_MFMA), moe.MOE_ERROR_NOT_SUPPORTED),
     (dict(path=5), moe.MOE_ERROR_INVALID_VALUE),
     (dict(dtype="f32", path=moe.MOE_PATH_FUSED), moe.MOE_ERROR_NOT_SUPPORTED),
-    (dict(path=moe.MOE_PATH_FUSED), moe.MOE_ERROR_NOT_SUPPORTED),   # switched off in this build
     (dict(flags=1), moe.MOE_ERROR_INVALID_VALUE),
 ])
 def test_plan_validation(kw, status):
@@ -68,6 +67,16 @@ def test_plan_struct_size_checked():
     cfg.struct_size = 40
     with pytest.raises(moe.MoEError):
         moe.moe_plan_create(cfg)
+
+
+def test_fused_plan_path():
+    plan, _ = moe.moe_plan_create(_cfg(path=moe.MOE_PATH_FUSED, max_tokens=128))
+    try:
+        assert moe.moe_plan_path(plan, 64, 8) == moe.MOE_PATH_FUSED
+        assert moe.moe_plan_path(plan, 1, 8) == moe.MOE_PATH_FUSED
+        assert moe.moe_plan_path(plan, 65, 8) == moe.MOE_PATH_STREAM  # past the fused batch limit
+    finally:
+        moe.moe_plan_destroy(plan)
 
 
 def test_workspace_sizing_and_path_choice():

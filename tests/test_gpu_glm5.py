@@ -176,6 +176,8 @@ def _fewer_tokens_than_planned(cfg, weights, path, max_tokens, calls):
                                              oracle.DTYPES[cfg.dtype], debug=True)
         _check_intermediates(cfg, g, tokens, dbg)
         check_outputs(cfg, small, workloads.torch_to_host(out)[tokens], delta, out_ref, tokens)
+        if moe.moe_plan_path(block.plan, T, cfg.k) == moe.MOE_PATH_FUSED:
+            assert block.fused_error(T) == 0
     block.close()
 
 
@@ -197,11 +199,15 @@ def test_glm5_plan_larger_than_call(glm5_weights, path, max_tokens, calls):
     _fewer_tokens_than_planned(cfg, glm5_weights, path, max_tokens, calls)
 
 
-@pytest.mark.skip(reason="the fused decode kernel is switched off: its first GPU run did not "
-                         "finish and the cause has not been established")
-def test_glm5_decode_fused(glm5_weights):
-    cfg = workloads.config("glm5_decode")
+@pytest.mark.parametrize("T", [64, 1])
+def test_glm5_decode_fused(glm5_weights, T):
+    cfg = workloads.config("glm5_decode", T=T)
     _check(cfg, glm5_weights, path=moe.MOE_PATH_FUSED)
+
+
+def test_glm5_fused_plan_for_8_tokens_called_with_fewer(glm5_weights):
+    cfg = workloads.config("glm5_decode", T=8)
+    _fewer_tokens_than_planned(cfg, glm5_weights, moe.MOE_PATH_FUSED, 8, (3, 8))
 
 
 def test_glm5_decode_mfma(glm5_weights):

@@ -187,11 +187,6 @@ def test_first_call_captured_in_a_graph(path):
 
 
 # ----------------------------------------------------------------------------- fused decode
-FUSED_OFF = ("the fused decode kernel is switched off: its first GPU run (case T=64 d=256 E=16 "
-             "I=192 Is=128 k=4) did not finish and the cause has not been established")
-
-
-@pytest.mark.skip(reason=FUSED_OFF)
 @pytest.mark.parametrize("shape", [
     dict(T=64, d=256, E=16, I=192, Is=128, k=4),           # several slices per expert
     dict(T=37, d=384, E=8, I=64, Is=192, k=2),              # odd T: a partial chunk
@@ -208,7 +203,6 @@ def test_fused_decode(shape):
     assert block.fused_error(cfg.T) == 0
 
 
-@pytest.mark.skip(reason=FUSED_OFF)
 def test_fused_repeatability_in_place_and_workspace_reuse():
     cfg, small, route, tin = prepare(workloads.config("tiny_fp32", dtype="bf16", T=64, E=16,
                                                       k=4, d=256, I=128, Is=128), seed=17)
