@@ -113,14 +113,14 @@ def measure_peaks(launches=10):
                    "independent v_mfma_f32_32x32x16_bf16; HIP events over %d launches" % launches}
 
 
-def run_workload(cfg, tin, steps, warmup):
+def run_workload(cfg, tin, steps, warmup, path=None):
     import torch
     import mixture_experts_transformer_rmsnorm_amd as moe
 
     weights = {k: tin[k] for k in ("norm_w", "router_w", "corr_bias", "gate_up", "down",
                                    "shared_gate", "shared_up", "shared_down")}
     block = moe.MoEBlock(weights, max_tokens=cfg.T, top_k=cfg.k, routed_scale=cfg.routed_scale,
-                         eps=cfg.eps)
+                         eps=cfg.eps, path=moe.MOE_PATH_AUTO if path is None else path)
     x = tin["x"]
     out = torch.empty_like(x)
     stream = torch.cuda.current_stream()
@@ -132,7 +132,9 @@ def run_workload(cfg, tin, steps, warmup):
     path = moe.moe_plan_path(block.plan, cfg.T, cfg.k)
 
     # timed region: K steps; HIP events on the forward's stream around the dominant kernel
-    moe.moe_set_stage_timing(block.plan, moe.stage_mask(DOMINANT))
+    # (the fused decode kernel runs every stage in its one launch)
+    dominant = "fused_decode" if path == moe.MOE_PATH_FUSED else DOMINANT
+    moe.moe_set_stage_timing(block.plan, moe.stage_mask(dominant))
     moe.moe_stage_times(block.plan)  # reset
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
@@ -159,7 +161,7 @@ def run_workload(cfg, tin, steps, warmup):
     elapsed = t1 - t0
     ms_step = 1e3 * elapsed / steps
     alg = algorithmic(cfg, counts)
-    gu_ms = stage_ms[DOMINANT] / max(calls, 1)
+    gu_ms = stage_ms[dominant] / max(calls, 1)
     gu_s = gu_ms * 1e-3
     hbm_t = alg["gu_bytes"] / (HBM_PEAK_GBS * 1e9)
     mfma_t = alg["gu_flops"] / (BF16_PEAK_TFLOPS * 1e12)
@@ -176,7 +178,7 @@ def run_workload(cfg, tin, steps, warmup):
         att = ATTAINABLE["hbm"] if roof["bound"] == "hbm" else ATTAINABLE["mfma"]
         roof["attainable"] = round(att, 1)
         roof["frac_of_attainable"] = round(achieved / att, 4)
-    roof.update(kernel=DOMINANT, kernel_ms=round(gu_ms, 4), algorithmic_bytes=alg["gu_bytes"],
+    roof.update(kernel=dominant, kernel_ms=round(gu_ms, 4), algorithmic_bytes=alg["gu_bytes"],
                 algorithmic_flops=alg["gu_flops"], active_experts=alg["n_active"])
     if roof["traffic"]:
         roof["traffic_over_algorithmic"] = round(roof["traffic"] / alg["gu_bytes"], 4)
@@ -426,9 +428,11 @@ def measure_configs(cfg, tin, steps, names=("glm5_prefill_zipf", "mid_prefill"))
     return out
 
 
-def measure_sweep(cfg, tin, steps, warmup, tokens=(1, 8, 16, 32, 128, 256)):
+def measure_sweep(cfg, tin, steps, warmup, tokens=(1, 8, 16, 32, 128, 256),
+                  fused_tokens=(1, 8, 64)):
     """The MoE block at other batch sizes on the same weights (decode-sized batches use
-    the streaming kernels): ms per step, tokens/s and the gate_up kernel's HBM rate."""
+    the streaming kernels): ms per step, tokens/s and the gate_up kernel's HBM rate;
+    and the fused single-launch decode kernel (MOE_PATH_FUSED) at decode batch sizes."""
     import torch
     import workloads
     out = {}
@@ -449,6 +453,22 @@ def measure_sweep(cfg, tin, steps, warmup, tokens=(1, 8, 16, 32, 128, 256)):
                           "gate_up_frac": r["roofline"]["frac"],
                           "active_experts": r["roofline"]["active_experts"]}
         log("sweep T=%d: %.4f ms/step, %.1f tokens/s" % (T, r["ms_per_step"], r["value"]))
+        del t2
+    import mixture_experts_transformer_rmsnorm_amd as moe
+    for T in fused_tokens:
+        c = workloads.config(cfg, T=T)
+        t2 = dict(tin)
+        sm = workloads.draw_small(c, 0)
+        for key in ("x", "norm_w", "router_w"):
+            t2[key] = workloads.host_to_torch(sm[key], c.dtype, "cuda")
+        t2["corr_bias"] = torch.from_numpy(sm["corr_bias"]).cuda()
+        r = run_workload(c, t2, steps, warmup, path=moe.MOE_PATH_FUSED)
+        out["fused_T%d" % T] = {"tokens": T, "ms_per_step": round(r["ms_per_step"], 4),
+                                "ms_per_step_median": round(r["ms_per_step_median"], 4),
+                                "tokens_per_s": round(r["value"], 1), "kernel_path": "fused",
+                                "step_GB_per_s": r["step_roofline"]["GB_per_s"],
+                                "step_frac": r["step_roofline"]["frac"]}
+        log("sweep fused T=%d: %.4f ms/step, %.1f tokens/s" % (T, r["ms_per_step"], r["value"]))
         del t2
     return out
 

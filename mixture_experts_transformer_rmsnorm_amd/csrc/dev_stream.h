@@ -31,10 +31,23 @@ __host__ __device__ constexpr int rs_strip_cols() {
 struct RsRange {
   int64_t total, C;
   int blocks, hblocks;
+  // (total - head) = q * (blocks - hblocks) + r: lo(b) = head + b' q + floor(b' r /
+  // (blocks - hblocks)) with b' = b - hblocks, so lo() needs one 32-bit division
+  // (the fixup evaluates it for every part it adds; a 64-bit division each was most
+  // of its time)
+  int64_t q;
+  int r;
+  __device__ __forceinline__ void split_rest() {
+    const int64_t rest = total - (int64_t)hblocks * C;
+    const int tb = blocks - hblocks;
+    q = tb > 0 ? rest / tb : 0;
+    r = tb > 0 ? (int)(rest - q * tb) : 0;
+  }
   __device__ __forceinline__ int64_t lo(int b) const {
     if (b <= hblocks) return (int64_t)b * C;
-    const int64_t head = (int64_t)hblocks * C;
-    return head + (int64_t)(b - hblocks) * (total - head) / (blocks - hblocks);
+    const int bb = b - hblocks;
+    return (int64_t)hblocks * C + (int64_t)bb * q +
+           (int64_t)((uint32_t)(bb * r) / (uint32_t)(blocks - hblocks));
   }
   // The block whose range holds chunk x: the largest b with lo(b) <= x.
   __device__ __forceinline__ int block_of(int64_t x) const {
@@ -72,6 +85,7 @@ struct RsGeom {
     } else {
       R.hblocks = R.blocks = (int)items;
     }
+    R.split_rest();
   }
 };
 
@@ -308,7 +322,7 @@ __device__ __forceinline__ void rs_finish(const GroupArgs& g, const StreamFix& f
     // The parts of U blocks at a time are loaded together (at one token an item
     // spans about 32 blocks, and one part after another took a load latency
     // each), then added in block order; blocks with an empty range hold no part.
-    constexpr int U = 8 / MT;  // 16 float4 of parts in flight per lane
+    constexpr int U = 16 / MT;  // 32 float4 of parts in flight per lane
     for (int bb0 = b; bb0 <= bl; bb0 += U) {
       float4 v[U][MT][V / 4];
       bool use[U];

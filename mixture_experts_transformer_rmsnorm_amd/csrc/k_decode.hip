@@ -25,11 +25,12 @@
 // (the routing's pass count, the active-expert count) reach every thread of a
 // block from one read by thread 0 through LDS.
 //
-// Grid barrier: each block's waves issue an agent-scope release fence, then
-// thread 0 adds 1 to a cumulative arrival counter (acquire-release, agent scope);
-// the block that brings it to blocks x (barriers passed + 1) publishes the next
-// generation number (release); the others' thread 0 polls the generation word.
-// Every thread then issues an agent-scope acquire fence.  Each wait is bounded by
+// Grid barrier: after a block barrier, wave 0 issues an agent-scope release fence
+// for the block, then thread 0 adds 1 to a cumulative arrival counter
+// (acquire-release, agent scope); the block that brings it to blocks x (barriers
+// passed + 1) publishes the next generation number (release); the others' thread
+// 0 polls the generation word.  Wave 0 then issues an agent-scope acquire fence
+// before a block barrier lets the other waves read.  Each wait is bounded by
 // wall-clock time (1 s of the 100 MHz constant clock): a wait that runs out, or
 // that sees the error flag already set, sets the flag, and its block leaves the
 // kernel at once, so every wait of every block ends and the launch completes;
@@ -68,8 +69,11 @@ struct FusedSmem {
 // Grid barrier (see the file comment); returns false when the block must leave.
 __device__ __forceinline__ bool grid_barrier(uint32_t* sync, uint32_t blocks, uint32_t& gen,
                                              int* bcast) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // Wave 0's fences act for the block: after the block barrier every wave's stores
+  // have reached this XCD's L2, which the release writes back; the acquire
+  // invalidates this compute unit's L1 and the L2's lines before any wave reads.
   __syncthreads();
+  if (threadIdx.x < kWave) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   if (threadIdx.x == 0) {
     const uint32_t target = gen + 1;
     int ok = __hip_atomic_load(sync + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;
@@ -93,8 +97,8 @@ __device__ __forceinline__ bool grid_barrier(uint32_t* sync, uint32_t blocks, ui
     if (!ok) __hip_atomic_fetch_or(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     bcast[0] = ok;
   }
+  if (threadIdx.x < kWave) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   gen += 1;
   const bool ok = bcast[0] != 0;
   __syncthreads();  // bcast is written again at the next barrier
