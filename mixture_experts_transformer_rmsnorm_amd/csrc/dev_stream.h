@@ -130,9 +130,11 @@ struct RsLane {
   int grp, ocol, spos, sgap;
   int64_t wcol;
   bool is_up, ok;
-  __device__ __forceinline__ RsLane(const GroupArgs& g, int n_out, int strip) {
+  // tid: the lane's index in a block of NTH lanes (its thread index, or in the
+  // fixup kernel, whose blocks are one wave each, wave w of the item's NTH lanes)
+  __device__ __forceinline__ RsLane(const GroupArgs& g, int n_out, int strip, int tid) {
     constexpr int V = Elem<T>::kVec, SW = rs_strip_cols<T, GU, NTH>();
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int lane = tid % kWave, wave = tid / kWave;
     is_up = GU && lane >= kWave / 2;
     grp = GU ? wave * (kWave / 2) + lane % (kWave / 2) : tid;
     ocol = strip * SW + grp * V;
@@ -281,7 +283,7 @@ __device__ __forceinline__ void rs_part(const GroupArgs& g, const StreamFix& fx,
                                         const T* __restrict__ Wall, const RsItem& it, int c0,
                                         int c1, int b, int64_t item0, T* __restrict__ out) {
   constexpr int V = Elem<T>::kVec;
-  const RsLane<T, GU, NTH> ln(g, G.n_out, it.strip);
+  const RsLane<T, GU, NTH> ln(g, G.n_out, it.strip, threadIdx.x);
   const T* W = Wall + (int64_t)it.e * G.K * G.ldw;
   float acc[MT][V];
   rs_accumulate<T, GU, MT, NTH>(g, A, G.K, W, G.ldw, it, ln, c0 * kRsChunk, c1 * kRsChunk, acc);
@@ -308,9 +310,9 @@ __device__ __forceinline__ void rs_part(const GroupArgs& g, const StreamFix& fx,
 template <typename T, bool GU, int MT, int NTH>
 __device__ __forceinline__ void rs_finish(const GroupArgs& g, const StreamFix& fx,
                                           const RsGeom<T, GU, NTH>& G, const RsItem& it, int b,
-                                          int64_t item0, T* __restrict__ out) {
+                                          int64_t item0, T* __restrict__ out, int tid) {
   constexpr int V = Elem<T>::kVec;
-  const RsLane<T, GU, NTH> ln(g, G.n_out, it.strip);
+  const RsLane<T, GU, NTH> ln(g, G.n_out, it.strip, tid);
   const int64_t ld = rs_slot_ld<T, GU, NTH>(G.n_out);
   const int bl = G.R.block_of(item0 + G.C - 1);
   float acc[MT][V];
@@ -391,12 +393,12 @@ __device__ __forceinline__ void rs_block(const GroupArgs& g, const StreamFix& fx
 }
 
 // Block b's fixup: finishes the item cut at the end of its range when the item
-// starts in that range (so each cut item is finished once).  No block barrier
-// inside.
+// starts in that range (so each cut item is finished once); tid as for RsLane.  No
+// block barrier inside.
 template <typename T, bool GU, int NTH>
 __device__ __forceinline__ void rs_fixup_block(const GroupArgs& g, const StreamFix& fx,
                                                const int* s_pass, int n_active,
-                                               T* __restrict__ out, int b, int blocks) {
+                                               T* __restrict__ out, int b, int blocks, int tid) {
   const RsGeom<T, GU, NTH> G(g, s_pass[n_active], blocks);
   if (b + 1 >= G.R.blocks) return;  // every block took whole items, or no successor
   const int64_t lo = G.R.lo(b), x = G.R.lo(b + 1);
@@ -405,7 +407,7 @@ __device__ __forceinline__ void rs_fixup_block(const GroupArgs& g, const StreamF
   if (item0 < lo) return;  // the item started in an earlier block, which finishes it
   int ai = 0;
   const RsItem it = rs_item<true>(g, s_pass, n_active, G.strips, item, &ai);
-#define MOE_FIN(MT) rs_finish<T, GU, MT, NTH>(g, fx, G, it, b, item0, out)
+#define MOE_FIN(MT) rs_finish<T, GU, MT, NTH>(g, fx, G, it, b, item0, out, tid)
   if (it.mt == 1) MOE_FIN(1);
   else if (it.mt == 2) MOE_FIN(2);
   else if (it.mt <= 4) MOE_FIN(4);

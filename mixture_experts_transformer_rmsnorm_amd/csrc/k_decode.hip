@@ -194,7 +194,7 @@ __device__ __attribute__((noinline)) void stream_part(GroupArgs g, StreamFix fx,
 template <bool GU>
 __device__ __attribute__((noinline)) void stream_fix(GroupArgs g, StreamFix fx, const int* s_pass,
                                                      int n_active, bf16* out, int b, int blocks) {
-  rs_fixup_block<bf16, GU, kFT>(g, fx, s_pass, n_active, out, b, blocks);
+  rs_fixup_block<bf16, GU, kFT>(g, fx, s_pass, n_active, out, b, blocks, threadIdx.x);
 }
 
 // Whether the streaming phase of this geometry cuts items between blocks (the

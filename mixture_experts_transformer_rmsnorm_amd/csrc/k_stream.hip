@@ -49,20 +49,26 @@ __global__ __launch_bounds__(rs_threads<GU>()) void stream_kernel(GroupArgs g, S
   rs_block<T, GU, rs_threads<GU>()>(g, fx, s_pass, n_active, A, Wall, out, blockIdx.x, fx.blocks);
 }
 
+// The fixup runs one wave per block: block x finishes the columns of wave x % W
+// (W = waves of the main kernel's blocks) of the item cut at the end of main block
+// x / W's range.  A cut item's parts are then added by W compute units at once,
+// not one (at one token an item spans about 32 parts, and one compute unit
+// adding a down item's 768 KiB of them took 27 us).
 template <typename T, bool GU>
-__global__ __launch_bounds__(rs_threads<GU>()) void stream_fixup_kernel(GroupArgs g,
-                                                                        StreamFix fx,
-                                                                        T* __restrict__ out) {
+__global__ __launch_bounds__(kWave) void stream_fixup_kernel(GroupArgs g, StreamFix fx,
+                                                             T* __restrict__ out) {
+  constexpr int W = rs_threads<GU>() / kWave;
   __shared__ int s_pass[kMaxStreamExperts + 1];
+  const int b = blockIdx.x / W, tid = (blockIdx.x % W) * kWave + threadIdx.x;
   {
     // nothing to finish when every block took whole items (or this block has no successor)
     const RsGeom<T, GU, rs_threads<GU>()> G0(g, g.hdr->n_passes, fx.blocks);
-    if ((int)blockIdx.x + 1 >= G0.R.blocks) return;
+    if (b + 1 >= G0.R.blocks) return;
   }
   const int n_active = g.hdr->n_active;
-  for (int i = threadIdx.x; i <= n_active; i += rs_threads<GU>()) s_pass[i] = g.pass_base[i];
+  for (int i = threadIdx.x; i <= n_active; i += kWave) s_pass[i] = g.pass_base[i];
   __syncthreads();
-  rs_fixup_block<T, GU, rs_threads<GU>()>(g, fx, s_pass, n_active, out, blockIdx.x, fx.blocks);
+  rs_fixup_block<T, GU, rs_threads<GU>()>(g, fx, s_pass, n_active, out, b, fx.blocks, tid);
 }
 
 // The partition assumes one block per compute unit (the dispatcher spreads the
@@ -106,8 +112,8 @@ static hipError_t launch_stream(const GroupArgs& g, const StreamFix& fx_in, cons
       g, fx, (const T*)A, (const T*)W, (T*)out);
   err = hipGetLastError();
   if (err != hipSuccess || fx.blocks == 1) return err;
-  stream_fixup_kernel<T, GU><<<dim3((unsigned)fx.blocks - 1), rs_threads<GU>(), 0, s>>>(
-      g, fx, (T*)out);
+  stream_fixup_kernel<T, GU><<<dim3((unsigned)(fx.blocks - 1) * (rs_threads<GU>() / kWave)), kWave, 0,
+                               s>>>(g, fx, (T*)out);
   return hipGetLastError();
 }
 
