@@ -18,7 +18,8 @@
  *    to the input dtype, then the per-feature gain; epsilon default 1e-6),
  *    "block" (GlmMoeDsaDecoderLayer: out = residual + mlp(norm(residual))) and
  *    "mlp" (GlmMoeDsaMLP: the SwiGLU form, bias-free linear maps).
- *  - "nemo_automodel ... glm4_moe.state_dict_adapter", Glm4MoeStateDictAdapter:
+ *  - "nemo_automodel.components.models.glm4_moe.state_dict_adapter",
+ *    class Glm4MoeStateDictAdapter:
  *    the grouped native expert layout gate_and_up_projs [n_experts, dim,
  *    2*moe_inter_dim] and down_projs [n_experts, moe_inter_dim, dim], and the
  *    shared expert's separate gate/up/down nn.Linear weights.
@@ -206,8 +207,8 @@ MOE_API moe_status_t moe_dense_block_forward(moe_plan_t plan, void* workspace, s
                                              const void* norm_w, const void* gate, const void* up,
                                              const void* down, void* out);
 
-/* Expert weight layout conversion ("nemo_automodel ... glm4_moe.state_dict_adapter",
- * Glm4MoeStateDictAdapter: HF checkpoints keep each expert's gate_proj, up_proj and
+/* Expert weight layout conversion ("nemo_automodel.components.models.glm4_moe.state_dict_adapter",
+ * class Glm4MoeStateDictAdapter: HF checkpoints keep each expert's gate_proj, up_proj and
  * down_proj as separate nn.Linear weights; the native grouped layout stacks them
  * as gate_and_up_projs [n_experts, dim, 2*moe_inter_dim] and down_projs
  * [n_experts, moe_inter_dim, dim]).  One expert per call (d = dim, I = inter):

@@ -1,7 +1,8 @@
 // Layout conversion of expert weights between the HF checkpoint layout (per expert,
 // nn.Linear [out, in]: gate_proj.weight [I, d], up_proj.weight [I, d],
 // down_proj.weight [d, I]) and the grouped layout of Glm4MoeStateDictAdapter
-// ("nemo_automodel ... glm4_moe.state_dict_adapter": gate_and_up_projs
+// (page "nemo_automodel.components.models.glm4_moe.state_dict_adapter",
+// class documentation: gate_and_up_projs
 // [E, d, 2I] with the gate columns first, down_projs [E, I, d]).  Pure data
 // movement: every conversion is a set of matrix transposes, bits copied as they are.
 //

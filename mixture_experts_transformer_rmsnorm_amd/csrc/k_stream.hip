@@ -2,7 +2,8 @@
 //
 // For decode-sized batches each active expert holds a handful of tokens, so the
 // expert matmuls are bound by reading the expert weights from HBM once.  The
-// weights stay in their grouped layout ("nemo_automodel ... state_dict_adapter",
+// weights stay in their grouped layout (page
+// "nemo_automodel.components.models.glm4_moe.state_dict_adapter", class
 // Glm4MoeStateDictAdapter: gate_and_up_projs [E, d, 2I] and down_projs [E, I, d],
 // both with the output dimension contiguous).
 //

@@ -261,8 +261,9 @@ def dense_block(x, norm_w, gate, up, down, dtype, eps=1e-6, debug=False):
 def pack_expert(gate, up, down):
     """Step O10: one expert's weights from the HF checkpoint layout (nn.Linear [out, in]:
     gate_proj.weight [I, d], up_proj.weight [I, d], down_proj.weight [d, I]) to the grouped
-    native layout of Glm4MoeStateDictAdapter: its slice of gate_and_up_projs [d, 2I] (gate
-    columns first, then up) and of down_projs [I, d].  Storage arrays of any dtype; the
+    native layout of class Glm4MoeStateDictAdapter (page
+    "nemo_automodel.components.models.glm4_moe.state_dict_adapter"): its slice of
+    gate_and_up_projs [d, 2I] (gate columns first, then up) and of down_projs [I, d].  Storage arrays of any dtype; the
     result holds the same elements, moved."""
     gate, up, down = (np.asarray(a) for a in (gate, up, down))
     I, d = gate.shape

@@ -19,7 +19,7 @@
  *          down(silu(gate x) * up x) with three bias-free linear maps.
  *   [BLK]  same page, excerpt "block" (GlmMoeDsaDecoderLayer): the residual is
  *          the pre-norm hidden state; out = residual + mlp(norm(residual)).
- *   [LAY]  "nemo_automodel...glm4_moe.state_dict_adapter", class
+ *   [LAY]  "nemo_automodel.components.models.glm4_moe.state_dict_adapter", class
  *          Glm4MoeStateDictAdapter: the grouped native layout
  *          gate_and_up_projs [n_experts, dim, 2*moe_inter_dim] and
  *          down_projs [n_experts, moe_inter_dim, dim]; the shared expert keeps

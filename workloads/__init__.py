@@ -5,7 +5,8 @@ It serves both the GPU library's tests / benchmark and the CPU oracle.
 
 Shapes follow the GLM-5 MoE block (hidden size 6144, 256 routed experts with
 moe_inter 2048, one shared expert of the same width; "GLM-5 · MoE transformer
-block", Parameters table) in the grouped-experts layout of
+block", Parameters table) in the grouped-experts layout that page
+"nemo_automodel.components.models.glm4_moe.state_dict_adapter" documents for class
 Glm4MoeStateDictAdapter (gate_and_up_projs [E, d, 2I], down_projs [E, I, d];
 shared expert as nn.Linear [out, in] weights).
 
