@@ -258,9 +258,9 @@ def _oracle_seconds(cfg, small, hosts, rows):
 def cpu_baseline(cfg, tin, small, seconds):
     """The CPU oracle, as it stands, timed on this machine's host cores.
 
-    Headline: the first tokens of the same decode batch, in chunks of 8 tokens until
-    about `seconds` of oracle time, on the oracle's OpenMP threads (the process's CPU
-    share).  Beside it: single-thread rates on the tiny fp32 workload (whole batch)
+    Headline: the same decode batch, in chunks of 8 tokens taken in order and from the
+    start again when the batch ends, until about `seconds` of oracle time, on the
+    oracle's OpenMP threads (the process's CPU share).  Beside it: single-thread rates on the tiny fp32 workload (whole batch)
     and on 4 decode tokens; and per-token rates on 16 tokens of the 4096-token prefill
     and of the mid-size workload, extrapolated to their whole batches."""
     import numpy as np
@@ -271,15 +271,21 @@ def cpu_baseline(cfg, tin, small, seconds):
     threads = oracle.num_threads()
     hosts = _HostExperts(cfg, tin)
     spent, done, chunk = 0.0, 0, 8
-    while done < cfg.T and (spent < seconds or done == 0):
-        rows = np.arange(done, min(cfg.T, done + chunk))
+    pos = 0
+    while spent < seconds or done == 0:
+        rows = np.arange(pos, min(cfg.T, pos + chunk))
         spent += _oracle_seconds(cfg, small, hosts, rows)
         done += len(rows)
+        pos = (pos + len(rows)) % cfg.T
         log("cpu oracle: %d tokens in %.1f s" % (done, spent))
+    if done >= cfg.T:
+        what = "%d tokens (%.2f passes over the %d %s tokens)" % (done, done / cfg.T, cfg.T,
+                                                                  cfg.name)
+    else:
+        what = "first %d of the %d %s tokens" % (done, cfg.T, cfg.name)
     res = {"value": round(done / spent, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-           "sample": "first %d of the %d %s tokens, full forward (norm, router, %d experts "
-                     "+ shared, combine), %.1f s on %d OpenMP threads" % (
-                         done, cfg.T, cfg.name, cfg.k, spent, threads),
+           "sample": "%s, full forward (norm, router, %d experts + shared, combine), "
+                     "%.1f s on %d OpenMP threads" % (what, cfg.k, spent, threads),
            "cpu_model": cpu_model(), "cores_available": len(os.sched_getaffinity(0))}
 
     # single thread: the tiny fp32 workload in full, and 4 decode tokens
