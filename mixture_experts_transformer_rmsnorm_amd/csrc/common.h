@@ -46,6 +46,7 @@ struct Elem<float> {
   }
   __device__ __forceinline__ static float round(float f) { return f; }
   __device__ __forceinline__ static float load1(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void store1(float* p, float f) { *p = f; }
 };
 
 template <>
@@ -64,6 +65,9 @@ struct Elem<bf16> {
   __device__ __forceinline__ static float round(float f) { return round_bf16(f); }
   __device__ __forceinline__ static float load1(const bf16* p, int64_t i) {
     return bf16_to_f32(p[i].bits);
+  }
+  __device__ __forceinline__ static void store1(bf16* p, float f) {
+    p->bits = (uint16_t)f32_to_bf16_bits(f);
   }
 };
 

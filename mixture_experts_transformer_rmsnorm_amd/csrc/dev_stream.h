@@ -17,6 +17,11 @@ constexpr int kRsChunk = 16;  // weight rows of the smallest K range
 template <bool GU>
 __host__ __device__ constexpr int rs_threads() { return GU ? 512 : 768; }
 
+// Consecutive weight rows a lane reads per step: 8 (gate_up) or 16 (down) 16-byte
+// vectors in flight per lane.
+template <bool GU>
+__host__ __device__ constexpr int rs_rows_per_step() { return GU ? 8 : 16; }
+
 // Output columns of one item (a strip): one 16-byte vector per lane for down;
 // for gate_up half the lanes read gate and half up columns.
 template <typename T, bool GU, int NTH>
@@ -166,17 +171,19 @@ __device__ __forceinline__ float dot2_bf16(uint32_t x, uint32_t y, float c) {
                                          __builtin_bit_cast(bf16x2_t, y), c, false);
 }
 
-// acc[m][c] = sum over weight rows [k0, k1) of A[row m][k] * W[k][wcol + c].
+// acc[m][c] = sum over the weight rows k0 + i * kstep + r (r < RPI, below k1) of
+// A[row m][k] * W[k][wcol + c]: the lane's runs of RPI consecutive rows, kstep
+// apart (kstep = RPI: every row of [k0, k1)), RPI weight vectors in flight per
+// lane.  LN: the lane's ok and wcol.
 //   gate_up: A = h [T, d] (rows gathered by perm_token), W = gate_up[e] [d, 2I]
 //   down:    A = act [rows, I],                          W = down[e] [I, d]
-template <typename T, bool GU, int MT, int NTH>
+template <typename T, bool GU, int MT, typename LN, int RPI = rs_rows_per_step<GU>()>
 __device__ __forceinline__ void rs_accumulate(const GroupArgs& g, const T* __restrict__ A,
                                               int64_t lda, const T* __restrict__ W, int64_t ldw,
-                                              const RsItem& it, const RsLane<T, GU, NTH>& ln, int k0,
-                                              int k1, float (&acc)[MT][Elem<T>::kVec]) {
+                                              const RsItem& it, const LN& ln, int k0, int k1,
+                                              int kstep, float (&acc)[MT][Elem<T>::kVec]) {
   constexpr int V = Elem<T>::kVec;
-  // rows per step: 8 (gate_up) or 16 (down) weight vectors in flight per lane
-  constexpr int RPI = GU ? 8 : 16;
+  static_assert(RPI % 8 == 0, "whole 16-byte activation vectors per step");
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -191,7 +198,7 @@ __device__ __forceinline__ void rs_accumulate(const GroupArgs& g, const T* __res
     arow[m] = A + r * lda;
   }
   const T* wp = W + (int64_t)k0 * ldw + ln.wcol;
-  for (int k = k0; k < k1; k += RPI, wp += (int64_t)RPI * ldw) {
+  for (int k = k0; k < k1; k += kstep, wp += (int64_t)kstep * ldw) {
     uint4 wv[RPI];
 #pragma unroll
     for (int r = 0; r < RPI; ++r) wv[r] = ldg16_stream(wp + (int64_t)r * ldw);
@@ -286,7 +293,8 @@ __device__ __forceinline__ void rs_part(const GroupArgs& g, const StreamFix& fx,
   const RsLane<T, GU, NTH> ln(g, G.n_out, it.strip, threadIdx.x);
   const T* W = Wall + (int64_t)it.e * G.K * G.ldw;
   float acc[MT][V];
-  rs_accumulate<T, GU, MT, NTH>(g, A, G.K, W, G.ldw, it, ln, c0 * kRsChunk, c1 * kRsChunk, acc);
+  rs_accumulate<T, GU, MT>(g, A, G.K, W, G.ldw, it, ln, c0 * kRsChunk, c1 * kRsChunk,
+                           rs_rows_per_step<GU>(), acc);
   if (c0 == 0 && c1 == G.C) {
     rs_store<T, GU, MT, NTH>(acc, it, ln, G.n_out, out);
     return;

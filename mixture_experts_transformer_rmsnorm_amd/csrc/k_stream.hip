@@ -72,6 +72,93 @@ __global__ __launch_bounds__(kWave) void stream_fixup_kernel(GroupArgs g, Stream
   rs_fixup_block<T, GU, rs_threads<GU>()>(g, fx, s_pass, n_active, out, b, fx.blocks, tid);
 }
 
+// Column split, for calls whose streaming passes (times the strips of a row) fill
+// at most half the resident blocks: no item is cut along K, so no partial sums and
+// no fixup.  Each pass's columns are split into J parts (J the largest power of
+// two, at most 32, with passes * strips * J <= blocks), and a block takes one (pass, part)
+// unit: all K weight rows of its columns.  Its lanes form J row groups of NTH / J
+// lanes; a lane reads runs of RPI consecutive rows, J * RPI rows apart, over the
+// part's columns (gate_up: the first half of a group's lanes read gate and the
+// second half the matching up columns), and the J groups' sums meet in LDS, one
+// token row at a time, for the epilogue.  At one token (8 passes, J = 32) a
+// gate_up unit reads 128 bytes of gate and 128 of up columns per weight row, a
+// down unit 384 bytes.
+struct ColLane {
+  bool ok, is_up;
+  int64_t wcol;
+};
+
+template <typename T, bool GU, int MT>
+__device__ __forceinline__ void cols_unit(const GroupArgs& g, const T* __restrict__ A,
+                                          const T* __restrict__ Wall, T* __restrict__ out,
+                                          const RsItem& it, int q, int J, float* s_red) {
+  // 8 rows in flight per lane for both products: the down blocks' 768 lanes leave
+  // at most 168 registers per lane, too few for 16 rows and 8 token rows
+  constexpr int NTH = rs_threads<GU>(), V = Elem<T>::kVec, RPI = 8;
+  const int K = GU ? g.d : g.I, n_out = GU ? g.I : g.d;
+  const int64_t ldw = GU ? 2 * (int64_t)g.I : (int64_t)g.d;
+  const int LPR = NTH / J;                     // lanes per weight row
+  const int SWJ = (GU ? LPR / 2 : LPR) * V;    // output columns of a part
+  const int tid = threadIdx.x, rg = tid / LPR, cl = tid % LPR;
+  ColLane ln;
+  ln.is_up = GU && cl >= LPR / 2;
+  const int ocol = q * SWJ + (GU ? cl % (LPR / 2) : cl) * V;
+  ln.ok = ocol < n_out;  // n_out is a multiple of V
+  ln.wcol = (ln.is_up ? (int64_t)g.I : 0) + ocol;
+  float acc[MT][V];
+  rs_accumulate<T, GU, MT, ColLane, RPI>(g, A, K, Wall + (int64_t)it.e * K * ldw, ldw, it, ln,
+                                         rg * RPI, K, J * RPI, acc);
+  // s_red[rg][cl * V + c]: a row group's sums, gate columns first (for gate_up)
+  const int vals = LPR * V;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m >= it.mt) break;  // the same for the whole block
+#pragma unroll
+    for (int c = 0; c < V; ++c) s_red[tid * V + c] = acc[m][c];
+    __syncthreads();
+    T* orow = out + (int64_t)(it.seg + it.m0 + m) * n_out;
+    for (int t = tid; t < SWJ; t += NTH) {
+      float a = 0.f, u = 0.f;
+      for (int r = 0; r < J; ++r) {
+        a += s_red[r * vals + t];
+        if (GU) u += s_red[r * vals + SWJ + t];
+      }
+      const int col = q * SWJ + t;
+      if (col < n_out) Elem<T>::store1(orow + col, GU ? silu(a) * u : a);
+    }
+    __syncthreads();
+  }
+}
+
+template <typename T, bool GU>
+__global__ __launch_bounds__(rs_threads<GU>()) void stream_cols_kernel(GroupArgs g, int blocks,
+                                                                       const T* __restrict__ A,
+                                                                       const T* __restrict__ Wall,
+                                                                       T* __restrict__ out) {
+  constexpr int NTH = rs_threads<GU>(), V = Elem<T>::kVec;
+  __shared__ int s_pass[kMaxStreamExperts + 1];
+  __shared__ float s_red[NTH * V];
+  const int n_active = g.hdr->n_active;
+  for (int i = threadIdx.x; i <= n_active; i += NTH) s_pass[i] = g.pass_base[i];
+  __syncthreads();
+  const int n_out = GU ? g.I : g.d;
+  const int strips = (n_out + rs_strip_cols<T, GU, NTH>() - 1) / rs_strip_cols<T, GU, NTH>();
+  const int64_t passes = (int64_t)s_pass[n_active] * strips;  // (pass, strip) pairs
+  int J = 1;
+  while (J < 32 && passes * J * 2 <= blocks) J *= 2;
+  const int64_t units = passes * J;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int64_t ps = u / J;
+    const int q = (int)(ps % strips) * J + (int)(u % J);  // column part within the pass
+    int ai = 0;
+    const RsItem it = rs_item<true>(g, s_pass, n_active, 1, ps / strips, &ai);
+    if (it.mt == 1) cols_unit<T, GU, 1>(g, A, Wall, out, it, q, J, s_red);
+    else if (it.mt == 2) cols_unit<T, GU, 2>(g, A, Wall, out, it, q, J, s_red);
+    else if (it.mt <= 4) cols_unit<T, GU, 4>(g, A, Wall, out, it, q, J, s_red);
+    else cols_unit<T, GU, 8>(g, A, Wall, out, it, q, J, s_red);
+  }
+}
+
 // The partition assumes one block per compute unit (the dispatcher spreads the
 // blocks of a launch over the CUs only when no CU can hold two), so each launch
 // asks for more dynamic LDS than half a CU's 160 KiB; the kernels do not use it.
@@ -102,13 +189,20 @@ static hipError_t resident_blocks(int* blocks) {
 }
 
 template <typename T, bool GU>
-static hipError_t launch_stream(const GroupArgs& g, const StreamFix& fx_in, const void* A,
-                                const void* W, void* out, hipStream_t s) {
+static hipError_t launch_stream(const GroupArgs& g, const StreamFix& fx_in, int64_t max_passes,
+                                const void* A, const void* W, void* out, hipStream_t s) {
   StreamFix fx = fx_in;
   hipError_t err = resident_blocks<T, GU>(&fx.blocks);
   if (err != hipSuccess) return err;
   if (fx.blocks < 1 || fx.blocks > kStreamMaxBlocks || g.E > kMaxStreamExperts)
     return hipErrorInvalidValue;
+  constexpr int SW = rs_strip_cols<T, GU, rs_threads<GU>()>();
+  const int64_t strips = ((GU ? g.I : g.d) + SW - 1) / SW;
+  if (2 * max_passes * strips <= fx.blocks) {  // J >= 2 whatever the routing
+    stream_cols_kernel<T, GU><<<dim3((unsigned)fx.blocks), rs_threads<GU>(), kRsLdsHold, s>>>(
+        g, fx.blocks, (const T*)A, (const T*)W, (T*)out);
+    return hipGetLastError();
+  }
   stream_kernel<T, GU><<<dim3((unsigned)fx.blocks), rs_threads<GU>(), kRsLdsHold, s>>>(
       g, fx, (const T*)A, (const T*)W, (T*)out);
   err = hipGetLastError();
@@ -119,15 +213,17 @@ static hipError_t launch_stream(const GroupArgs& g, const StreamFix& fx_in, cons
 }
 
 hipError_t launch_stream_gate_up(int dtype, const GroupArgs& g, const StreamFix& fx,
-                                 const void* h, const void* gate_up, void* act, hipStream_t s) {
-  if (dtype == kBF16) return launch_stream<bf16, true>(g, fx, h, gate_up, act, s);
-  return launch_stream<float, true>(g, fx, h, gate_up, act, s);
+                                 int64_t max_passes, const void* h, const void* gate_up,
+                                 void* act, hipStream_t s) {
+  if (dtype == kBF16) return launch_stream<bf16, true>(g, fx, max_passes, h, gate_up, act, s);
+  return launch_stream<float, true>(g, fx, max_passes, h, gate_up, act, s);
 }
 
 hipError_t launch_stream_down(int dtype, const GroupArgs& g, const StreamFix& fx,
-                              const void* act, const void* down, void* y, hipStream_t s) {
-  if (dtype == kBF16) return launch_stream<bf16, false>(g, fx, act, down, y, s);
-  return launch_stream<float, false>(g, fx, act, down, y, s);
+                              int64_t max_passes, const void* act, const void* down, void* y,
+                              hipStream_t s) {
+  if (dtype == kBF16) return launch_stream<bf16, false>(g, fx, max_passes, act, down, y, s);
+  return launch_stream<float, false>(g, fx, max_passes, act, down, y, s);
 }
 
 }  // namespace moe

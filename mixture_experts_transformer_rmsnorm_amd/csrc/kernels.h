@@ -156,12 +156,16 @@ struct StreamFix {
   int blocks;           // set by the launcher: resident blocks, at most kStreamMaxBlocks
 };
 
-// act[row][n] = D(silu(h[tok] . G[:, n]) * (h[tok] . G[:, I + n]))  for every permuted row
+// act[row][n] = D(silu(h[tok] . G[:, n]) * (h[tok] . G[:, I + n]))  for every permuted row.
+// max_passes: an upper bound of the call's streaming passes (T * k); when it fits
+// the resident blocks the column split runs (no partial sums, no fixup).
 hipError_t launch_stream_gate_up(int dtype, const GroupArgs& g, const StreamFix& fx,
-                                 const void* h, const void* gate_up, void* act, hipStream_t s);
+                                 int64_t max_passes, const void* h, const void* gate_up,
+                                 void* act, hipStream_t s);
 // y[row][c] = D(act[row] . down[e][:, c])
 hipError_t launch_stream_down(int dtype, const GroupArgs& g, const StreamFix& fx,
-                              const void* act, const void* down, void* y, hipStream_t s);
+                              int64_t max_passes, const void* act, const void* down, void* y,
+                              hipStream_t s);
 
 // rows: T * k, the permuted rows of the call (it picks the weight loads' cache policy)
 hipError_t launch_mfma_gate_up(const GroupArgs& g, int max_mtiles, int64_t rows, const void* h,

@@ -662,11 +662,11 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   const int max_mtiles = (int)(cdiv(A, kGroupBM) + std::min<int64_t>(E, A));
   stage(kStGateUp, [&] {
     return mfma ? launch_mfma_gate_up(g, max_mtiles, A, h, gate_up, act, s)
-                : launch_stream_gate_up(dt, g, fx, h, gate_up, act, s);
+                : launch_stream_gate_up(dt, g, fx, A, h, gate_up, act, s);
   });
   stage(kStDown, [&] {
     return mfma ? launch_mfma_down(g, max_mtiles, act, down, y, s)
-                : launch_stream_down(dt, g, fx, act, down, y, s);
+                : launch_stream_down(dt, g, fx, A, act, down, y, s);
   });
   if (side) {
     const hipError_t e2 = hipStreamWaitEvent(s, side->join, 0);

@@ -137,11 +137,11 @@ def test_glm5_decode_stream(glm5_weights):
     _check(cfg, glm5_weights, path=moe.MOE_PATH_STREAM)
 
 
-@pytest.mark.parametrize("T", [1, 8])
+@pytest.mark.parametrize("T", [1, 2, 8, 32])
 def test_glm5_decode_small_batches(glm5_weights, T):
-    """1 and 8 tokens: fewer (expert, pass) items than half the resident blocks, so
-    the streaming kernels split every item over several blocks (equal ranges) and
-    the fixup kernel finishes them all."""
+    """1 to 32 tokens: at most as many (expert, pass) items as resident blocks, so the
+    streaming kernels split each item's columns over J blocks (J = 32, 16, 4 and 1
+    here) and sum each block's row groups in LDS; no partial sums, no fixup."""
     cfg = workloads.config("glm5_decode", T=T)
     _check(cfg, glm5_weights, path=moe.MOE_PATH_AUTO)
 
