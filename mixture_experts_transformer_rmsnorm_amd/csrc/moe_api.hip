@@ -70,10 +70,11 @@ struct Split {
 // partial sums cost HBM traffic twice, in the product and in its consumer: a
 // 384-tile product split in two fills its last wave but the step is slower).
 // The 64-row kernel, one block per compute unit too and bound by its weight
-// stream, takes the split count with the fewest K-steps on the busiest compute
-// unit, a split's partial sums (M x 128 fp32 per tile, written and read again)
-// counting as 4M / 64 K-steps of weight traffic spread over all of them.
-Split nt_split(int64_t M, int64_t N, int64_t K, int tm, int tn, int tk, int max_splits) {
+// stream, takes the split count with the fewest K-steps on the busiest of `cus`
+// compute units, a split's partial sums (M x 128 fp32 per tile, written and read
+// again) counting as 4M / 64 K-steps of weight traffic spread over all of them.
+Split nt_split(int64_t M, int64_t N, int64_t K, int tm, int tn, int tk, int max_splits,
+               int cus = kComputeUnits) {
   const int64_t tiles = std::max<int64_t>(1, cdiv(M, tm) * cdiv(N, tn));
   const int64_t nkt = K / tk;
   const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(max_splits, nkt / 2));
@@ -83,9 +84,9 @@ Split nt_split(int64_t M, int64_t N, int64_t K, int tm, int tn, int tk, int max_
   } else if (tm == kNtSkinnyRows) {
     double best = 0.0;
     for (int64_t c = 1; c <= smax; ++c) {
-      const double est = (double)cdiv(tiles * c, kComputeUnits) * (double)cdiv(nkt, c) +
+      const double est = (double)cdiv(tiles * c, cus) * (double)cdiv(nkt, c) +
                          4.0 * (double)std::min<int64_t>(M, tm) / tk * (double)(tiles * c) /
-                             kComputeUnits;
+                             cus;
       if (c == 1 || est < best) {
         best = est;
         s = c;
@@ -156,6 +157,24 @@ bool use_fused(const moe_plan* p, int64_t T, int k) {
          p->cfg.n_experts > 0 && T <= kFusedMaxTokens;
 }
 
+// Compute units the shared expert's 64-row products are sized for when they run on
+// the side stream beside the routing steps: a quarter of the chip, so that the
+// routing kernels (one to a few blocks each, on the critical path) find free
+// compute units at once instead of waiting for a wave of the shared expert's
+// blocks (GLM-5 decode: 1 token 0.169 -> 0.159 ms, 2 tokens 0.250 -> 0.241 ms;
+// with half the chip 0.161 ms, with an eighth 0.172 ms).
+constexpr int kSideCUs = kComputeUnits / 4;
+
+// Compute units the shared expert's split-K is chosen for in a call of T tokens
+// and top-k k: kSideCUs when the call forks it onto the side stream (streaming
+// kernels), else the whole chip.
+int shared_cus(const moe_plan* p, int64_t T, int k) {
+  return p->cfg.n_experts > 0 && p->cfg.shared_inter > 0 && !use_mfma(p, T, k) &&
+                 !use_fused(p, T, k)
+             ? kSideCUs
+             : kComputeUnits;
+}
+
 // Tile sizes of the dense K-contiguous products of T rows for this plan's dtype.
 void nt_tiles(const moe_plan* p, int64_t T, int* tm, int* tn, int* tk) {
   if (p->cfg.dtype == MOE_DTYPE_BF16) {
@@ -172,15 +191,21 @@ void nt_tiles(const moe_plan* p, int64_t T, int* tm, int* tn, int* tk) {
 // split count depends only on the tile count, which is constant between
 // multiples of the row tile (128 or 256 rows), where the buffer is largest: the
 // multiples of 32 and Tmax itself cover the rest.
+// For the shared expert's products (shared = true) both compute-unit counts of
+// shared_cus are evaluated.
 constexpr int64_t kExactRows = 512;
-size_t max_partial_elems(const moe_plan* p, int64_t Tmax, int64_t N, int64_t K, int max_splits) {
+size_t max_partial_elems(const moe_plan* p, int64_t Tmax, int64_t N, int64_t K, int max_splits,
+                         bool shared) {
   size_t best = 0;
   const int64_t top = std::max<int64_t>(Tmax, 1);
   auto at = [&](int64_t T) {
     int tm, tn, tk;
     nt_tiles(p, T, &tm, &tn, &tk);
-    const Split s = nt_split(T, N, K, tm, tn, tk, max_splits);
-    best = std::max(best, (size_t)s.splits * (size_t)T * (size_t)N);
+    for (int cus : {kComputeUnits, kSideCUs}) {
+      if (cus != kComputeUnits && !shared) break;
+      const Split s = nt_split(T, N, K, tm, tn, tk, max_splits, cus);
+      best = std::max(best, (size_t)s.splits * (size_t)T * (size_t)N);
+    }
   };
   for (int64_t T = 1; T <= std::min(top, kExactRows); ++T) at(T);
   for (int64_t T = kExactRows + 32; T < top; T += 32) at(T);
@@ -202,7 +227,7 @@ void make_layout(moe_plan* p) {
   };
   Layout& L = p->lay;
   L.h = take((size_t)T * c.dim * es);
-  L.logits_bytes = max_partial_elems(p, T, c.n_experts, c.dim, kMaxRouterSplits) * 4;
+  L.logits_bytes = max_partial_elems(p, T, c.n_experts, c.dim, kMaxRouterSplits, false) * 4;
   L.logits = take(L.logits_bytes);
   L.topk_idx = take((size_t)A * 4);
   L.topk_w = take((size_t)A * 4);
@@ -223,10 +248,11 @@ void make_layout(moe_plan* p) {
   L.act = take((size_t)A * c.moe_inter * es);
   L.y = take((size_t)A * c.dim * es);
   if (c.shared_inter > 0) {
-    L.sh_gu_bytes = max_partial_elems(p, T, 2 * (int64_t)c.shared_inter, c.dim, kMaxSharedSplits) * 4;
+    L.sh_gu_bytes =
+        max_partial_elems(p, T, 2 * (int64_t)c.shared_inter, c.dim, kMaxSharedSplits, true) * 4;
     L.sh_gu = take(L.sh_gu_bytes);
     L.act_s = take((size_t)T * c.shared_inter * es);
-    L.sh_dn_bytes = max_partial_elems(p, T, c.dim, c.shared_inter, kMaxSharedSplits) * 4;
+    L.sh_dn_bytes = max_partial_elems(p, T, c.dim, c.shared_inter, kMaxSharedSplits, true) * 4;
     L.sh_dn = take(L.sh_dn_bytes);
   } else {
     L.sh_gu = L.act_s = L.sh_dn = 0;
@@ -239,20 +265,22 @@ void make_layout(moe_plan* p) {
 // The split-K partial sums a call of T rows writes fit the regions the plan sized
 // for max_tokens (WORKSPACE_TOO_SMALL otherwise; checked before anything is
 // enqueued, so a sizing mistake can never write past a region).
-moe_status_t check_splits(const moe_plan* p, int64_t T) {
+moe_status_t check_splits(const moe_plan* p, int64_t T, int k) {
   const moe_config_t& c = p->cfg;
   if (T <= 0) return MOE_SUCCESS;
   int tm, tn, tk;
   nt_tiles(p, T, &tm, &tn, &tk);
-  auto fits = [&](int64_t N, int64_t K, int max_splits, size_t bytes) {
-    const Split s = nt_split(T, N, K, tm, tn, tk, max_splits);
+  const int scus = shared_cus(p, T, k);
+  auto fits = [&](int64_t N, int64_t K, int max_splits, size_t bytes, int cus) {
+    const Split s = nt_split(T, N, K, tm, tn, tk, max_splits, cus);
     return (size_t)s.splits * (size_t)T * (size_t)N * 4 <= bytes;
   };
-  if (c.n_experts > 0 && !fits(c.n_experts, c.dim, kMaxRouterSplits, p->lay.logits_bytes))
+  if (c.n_experts > 0 &&
+      !fits(c.n_experts, c.dim, kMaxRouterSplits, p->lay.logits_bytes, kComputeUnits))
     return MOE_ERROR_WORKSPACE_TOO_SMALL;
   if (c.shared_inter > 0 &&
-      (!fits(2 * (int64_t)c.shared_inter, c.dim, kMaxSharedSplits, p->lay.sh_gu_bytes) ||
-       !fits(c.dim, c.shared_inter, kMaxSharedSplits, p->lay.sh_dn_bytes)))
+      (!fits(2 * (int64_t)c.shared_inter, c.dim, kMaxSharedSplits, p->lay.sh_gu_bytes, scus) ||
+       !fits(c.dim, c.shared_inter, kMaxSharedSplits, p->lay.sh_dn_bytes, scus)))
     return MOE_ERROR_WORKSPACE_TOO_SMALL;
   return MOE_SUCCESS;
 }
@@ -440,7 +468,7 @@ moe_status_t moe_plan_check(moe_plan_t p, int64_t T, int32_t k) {
   if (T < 0 || T > c.max_tokens) return MOE_ERROR_INVALID_VALUE;
   if (c.n_experts == 0 ? k != 0 : (k < 1 || k > c.max_top_k || k > c.n_experts))
     return MOE_ERROR_INVALID_VALUE;
-  return check_splits(p, T);
+  return check_splits(p, T, k);
 }
 
 moe_status_t moe_set_stage_timing(moe_plan_t p, int32_t stage_mask) {
@@ -499,7 +527,7 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
     return MOE_ERROR_MISALIGNED;
   if (workspace_bytes < p->lay.total) return MOE_ERROR_WORKSPACE_TOO_SMALL;
   {
-    const moe_status_t st = check_splits(p, T);
+    const moe_status_t st = check_splits(p, T, k);
     if (st != MOE_SUCCESS) return st;
   }
 
@@ -560,16 +588,17 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
     }
   };
   auto nt = [&](const void* Aop, int64_t lda, const void* B1, const void* B2, int64_t ldb,
-                int n_split, float* outp, int64_t N, int64_t K, int max_splits) {
-    const Split sp = nt_split(T, N, K, tm, tn, tk, max_splits);
+                int n_split, float* outp, int64_t N, int64_t K, const Split& sp) {
     NtArgs a{Aop, lda, B1, B2, ldb, n_split, outp, (int)T, (int)N, (int)K, sp.splits, sp.kt_per};
     return dt == kBF16 ? launch_mfma_nt(a, cs) : launch_fma_nt(dt, a, cs);
   };
   const Split rsplit = nt_split(T, E, d, tm, tn, tk, kMaxRouterSplits);
+  const int scus = shared_cus(p, T, k);
   const Split sdsplit =
-      has_shared ? nt_split(T, d, Is, tm, tn, tk, kMaxSharedSplits) : Split{0, 0};
+      has_shared ? nt_split(T, d, Is, tm, tn, tk, kMaxSharedSplits, scus) : Split{0, 0};
   const Split sgsplit =
-      has_shared ? nt_split(T, 2 * (int64_t)Is, d, tm, tn, tk, kMaxSharedSplits) : Split{0, 0};
+      has_shared ? nt_split(T, 2 * (int64_t)Is, d, tm, tn, tk, kMaxSharedSplits, scus)
+                 : Split{0, 0};
 
   if (use_fused(p, T, k)) {
     FusedArgs f{};
@@ -611,13 +640,13 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
         NtArgs a{h, d, shared_gate, shared_up, d, Is, nullptr, (int)T, 2 * Is, d, 1, sgsplit.kt_per};
         return launch_mfma_nt_swiglu(a, act_s, cs);
       }
-      return nt(h, d, shared_gate, shared_up, d, Is, sh_gu, 2 * (int64_t)Is, d, kMaxSharedSplits);
+      return nt(h, d, shared_gate, shared_up, d, Is, sh_gu, 2 * (int64_t)Is, d, sgsplit);
     });
     if (!fused_act)
       stage(kStSharedAct,
             [&] { return launch_swiglu_finalize(dt, sh_gu, sgsplit.splits, T, Is, act_s, cs); });
     stage(kStSharedDown, [&] {
-      return nt(act_s, Is, shared_down, shared_down, Is, d, sh_dn, d, Is, kMaxSharedSplits);
+      return nt(act_s, Is, shared_down, shared_down, Is, d, sh_dn, d, Is, sdsplit);
     });
   };
   auto fork_shared = [&] {
@@ -637,7 +666,7 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   };
   if (!mfma) fork_shared();
   stage(kStRouter,
-        [&] { return nt(h, d, router_w, router_w, d, E, logits, E, d, kMaxRouterSplits); });
+        [&] { return nt(h, d, router_w, router_w, d, E, logits, E, d, rsplit); });
   // Small batches: per-token selection blocks, then the whole permutation in one
   // block; otherwise chunked selection with histograms, scans and the scatter.
   const bool small_route = T * k <= kRouteSmallMax && E <= 1024;
@@ -712,7 +741,7 @@ moe_status_t moe_dense_block_forward(moe_plan_t p, void* workspace, size_t works
     return MOE_ERROR_MISALIGNED;
   if (workspace_bytes < p->lay.total) return MOE_ERROR_WORKSPACE_TOO_SMALL;
   {
-    const moe_status_t st = check_splits(p, T);
+    const moe_status_t st = check_splits(p, T, 0);
     if (st != MOE_SUCCESS) return st;
   }
 
