@@ -203,6 +203,17 @@ def run_workload(cfg, tin, steps, warmup, path=None):
                 max_load=int(counts.max()), counts=counts)
 
 
+def load_summary(counts):
+    """Tokens per expert of the timed batch: active experts and the spread of their loads."""
+    import numpy as np
+    c = np.asarray(counts)
+    nz = np.sort(c[c > 0])
+    if nz.size == 0:
+        return {"active_experts": 0}
+    return {"active_experts": int(nz.size), "min": int(nz[0]), "median": float(np.median(nz)),
+            "max": int(nz[-1]), "p90": float(np.percentile(nz, 90))}
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -614,6 +625,10 @@ def main():
     }
     if peaks:
         line["attainable"] = peaks
+    line["expert_load"] = load_summary(res["counts"])
+    props = torch.cuda.get_device_properties(0)
+    line["env"] = {"device": props.name, "compute_units": props.multi_processor_count,
+                   "torch": torch.__version__, "hip": torch.version.hip}
     if args.secondary:
         cfg2 = workloads.config(args.secondary)
         if (cfg2.d, cfg2.E, cfg2.I, cfg2.Is, cfg2.dtype) == (cfg.d, cfg.E, cfg.I, cfg.Is, cfg.dtype):
@@ -634,7 +649,8 @@ def main():
                                  "ms_per_step_min": round(r2["ms_per_step_min"], 4),
                                  "kernel_path": "stream" if r2["path"] == 1 else "mfma",
                                  "roofline": r2["roofline"], "step_roofline": r2["step_roofline"],
-                                 "stage_ms": r2["stage_ms"]}
+                                 "stage_ms": r2["stage_ms"],
+                                 "expert_load": load_summary(r2["counts"])}
             del tin2
     if extras_req:
         line["extras"] = run_extras(cfg, tin)

@@ -62,6 +62,11 @@
  *    enqueued; on error nothing is written and a status is returned.  Device
  *    faults surface at the caller's next synchronisation.  Inputs must be
  *    finite; NaN/Inf behaviour is unspecified.
+ *  - Debugging: with MOE_DEBUG_SYNC=1 in the environment (read at every call),
+ *    moe_block_forward and moe_dense_block_forward synchronise their stream
+ *    after each stage, so a kernel that fails is reported as MOE_ERROR_HIP by
+ *    the call that launched it.  It serialises the call and must not be set
+ *    while a stream is being captured into a graph.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

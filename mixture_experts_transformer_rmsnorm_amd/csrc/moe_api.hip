@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -287,6 +288,15 @@ moe_status_t check_splits(const moe_plan* p, int64_t T, int k) {
 
 bool misaligned(const void* ptr) { return ((uintptr_t)ptr & 15u) != 0; }
 
+// MOE_DEBUG_SYNC=1 in the environment (read at every forward call): each stage is
+// followed by a synchronisation of its stream, so that a kernel that fails is
+// reported by the call that launched it, as MOE_ERROR_HIP.  Debug only: it
+// serialises the forward, and a stream under graph capture cannot be synchronised.
+bool debug_sync() {
+  const char* v = getenv("MOE_DEBUG_SYNC");
+  return v && v[0] == '1' && v[1] == 0;
+}
+
 // Calls whose selected stages the event pool made by moe_set_stage_timing covers
 // (two events per stage and call); a call made while the pool is short is not
 // timed and not counted.
@@ -566,6 +576,7 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   const int32_t tmask = begin_timing(p, tlock);
   hipError_t err = hipSuccess;
   hipStream_t cs = s;  // stream the stages below are enqueued on
+  const bool dbg = debug_sync();
   auto stage = [&](int st, auto&& fn) {
     if (err != hipSuccess) return;
     EventPair ev{st, nullptr, nullptr};
@@ -581,6 +592,7 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
       if (err != hipSuccess) return;
     }
     err = fn();
+    if (err == hipSuccess && dbg) err = hipStreamSynchronize(cs);
     if (timing) {
       const hipError_t e2 = hipEventRecord(ev.b, cs);
       if (err == hipSuccess) err = e2;
@@ -767,6 +779,7 @@ moe_status_t moe_dense_block_forward(moe_plan_t p, void* workspace, size_t works
   std::unique_lock<std::mutex> tlock;
   const int32_t tmask = begin_timing(p, tlock);
   hipError_t err = hipSuccess;
+  const bool dbg = debug_sync();
   auto stage = [&](int st, auto&& fn) {
     if (err != hipSuccess) return;
     EventPair ev{st, nullptr, nullptr};
@@ -782,6 +795,7 @@ moe_status_t moe_dense_block_forward(moe_plan_t p, void* workspace, size_t works
       if (err != hipSuccess) return;
     }
     err = fn();
+    if (err == hipSuccess && dbg) err = hipStreamSynchronize(s);
     if (timing) {
       const hipError_t e2 = hipEventRecord(ev.b, s);
       if (err == hipSuccess) err = e2;

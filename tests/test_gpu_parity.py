@@ -222,3 +222,18 @@ def test_fused_repeatability_in_place_and_workspace_reuse():
     assert block.fused_error(T2) == 0
     delta, out_ref = oracle_outputs(cfg, small, route, tin, np.arange(T2))
     check_outputs(cfg, small, workloads.torch_to_host(out), delta, out_ref, np.arange(T2))
+
+
+def test_debug_sync_gives_the_same_result(monkeypatch):
+    """MOE_DEBUG_SYNC=1 synchronises after every stage (streaming path, with its side
+    stream, and the MFMA path); the results are those of a normal call, bit for bit."""
+    for path in (STREAM, MFMA):
+        cfg = workloads.config("tiny_fp32", dtype="bf16", T=40, d=256, E=16, I=128, Is=128, k=4)
+        cfg, small, route, tin = prepare(cfg, seed=29)
+        monkeypatch.delenv("MOE_DEBUG_SYNC", raising=False)
+        block, ref = run_gpu(cfg, tin, path)
+        monkeypatch.setenv("MOE_DEBUG_SYNC", "1")
+        _, got = run_gpu(cfg, tin, path, block=block)
+        monkeypatch.delenv("MOE_DEBUG_SYNC")
+        assert torch.equal(got, ref)
+        block.close()
