@@ -542,6 +542,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="glm5_decode")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="run the --config workload at this many tokens instead (named "
+                         "<config>_<tokens>tok), e.g. to profile a small decode batch")
     ap.add_argument("--secondary", default="glm5_prefill",
                     help="second workload of the same shape family reported in the line ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -598,6 +601,8 @@ def main():
         print(json.dumps({"extras": run_extras()}), flush=True)
         return
     cfg = workloads.config(args.config)
+    if args.tokens:
+        cfg = workloads.config(cfg, T=args.tokens, name="%s_%dtok" % (cfg.name, args.tokens))
     log("drawing %s inputs on the device" % cfg.name)
     tin = workloads.make_torch(cfg, 0, device="cuda", weights="device")
     small = workloads.draw_small(cfg, 0)
