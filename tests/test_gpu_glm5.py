@@ -5,7 +5,8 @@ outputs (out, delta) and the intermediates act and y of every (token, expert)
 pair on every token for the decode batch, and on a seeded, stratified sample of
 512 tokens (computed one by one by the oracle) for the prefill batches: every
 256-row M-tile of the hottest expert, the last M-tile of the 8 busiest, the
-rarest non-empty experts, the first and last token, the rest uniform.  Plans sized
+rarest non-empty experts, the first and last token, the rest uniform.  For the
+4096-token prefill, out and delta are checked on every token as well.  Plans sized
 for more tokens than a call passes are checked too, with a guard region after
 the workspace that must stay untouched."""
 import numpy as np
@@ -103,7 +104,7 @@ def _check_intermediates(cfg, g, tokens, dbg):
                        "y")
 
 
-def _check(cfg, weights, path=moe.MOE_PATH_AUTO, n_sample=None):
+def _check(cfg, weights, path=moe.MOE_PATH_AUTO, n_sample=None, all_outputs=False):
     small, route, tin = _inputs(cfg, weights)
     say("%s: forward on the GPU (path %d)" % (cfg.name, path))
     block, out = run_gpu(cfg, tin, path)
@@ -124,8 +125,16 @@ def _check(cfg, weights, path=moe.MOE_PATH_AUTO, n_sample=None):
                                          gu, dn, sh[0], sh[1], sh[2], oracle.DTYPES[cfg.dtype],
                                          debug=True)
     _check_intermediates(cfg, g, tokens, dbg)
-    got = workloads.torch_to_host(out)[tokens]
-    check_outputs(cfg, small, got, delta, out_ref, tokens)
+    host_out = workloads.torch_to_host(out)
+    check_outputs(cfg, small, host_out[tokens], delta, out_ref, tokens)
+    if all_outputs and n_sample is not None:
+        # out and delta of every token (no intermediates: they would not fit in memory)
+        every = np.arange(cfg.T)
+        gu, dn, sh = weights.host_experts(cfg, np.unique(route["idx"]))
+        say("  oracle on all %d tokens (outputs only)" % cfg.T)
+        delta, out_ref = oracle.experts(every, small["x"], route["h"], route["idx"], route["w"], gu,
+                                        dn, sh[0], sh[1], sh[2], oracle.DTYPES[cfg.dtype])
+        check_outputs(cfg, small, host_out, delta, out_ref, every)
     if moe.moe_plan_path(block.plan, cfg.T, cfg.k) == moe.MOE_PATH_FUSED:
         assert block.fused_error(cfg.T) == 0
     del block
@@ -216,7 +225,8 @@ def test_glm5_decode_mfma(glm5_weights):
 
 
 def test_glm5_prefill(glm5_weights):
-    _check(workloads.config("glm5_prefill"), glm5_weights, n_sample=N_SAMPLE)
+    """4096 tokens: intermediates on the stratified sample, out and delta on every token."""
+    _check(workloads.config("glm5_prefill"), glm5_weights, n_sample=N_SAMPLE, all_outputs=True)
 
 
 def test_glm5_prefill_zipf(glm5_weights):
