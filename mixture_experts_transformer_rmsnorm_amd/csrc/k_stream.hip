@@ -75,7 +75,8 @@ __global__ __launch_bounds__(kWave) void stream_fixup_kernel(GroupArgs g, Stream
 // Column split, for calls whose streaming passes (times the strips of a row) fill
 // at most half the resident blocks: no item is cut along K, so no partial sums and
 // no fixup.  Each pass's columns are split into J parts (J the largest power of
-// two, at most 32, with passes * strips * J <= blocks), and a block takes one (pass, part)
+// two, at most 32, with passes * strips * P(J) <= blocks, P(J) the parts that hold
+// columns: J at the GLM-5 widths), and a block takes one (pass, part)
 // unit: all K weight rows of its columns.  Its lanes form J row groups of NTH / J
 // lanes; a lane reads runs of RPI consecutive rows, J * RPI rows apart, over the
 // part's columns (gate_up: the first half of a group's lanes read gate and the
@@ -142,14 +143,22 @@ __global__ __launch_bounds__(rs_threads<GU>()) void stream_cols_kernel(GroupArgs
   for (int i = threadIdx.x; i <= n_active; i += NTH) s_pass[i] = g.pass_base[i];
   __syncthreads();
   const int n_out = GU ? g.I : g.d;
-  const int strips = (n_out + rs_strip_cols<T, GU, NTH>() - 1) / rs_strip_cols<T, GU, NTH>();
+  constexpr int SW = rs_strip_cols<T, GU, NTH>();
+  const int strips = (n_out + SW - 1) / SW;
   const int64_t passes = (int64_t)s_pass[n_active] * strips;  // (pass, strip) pairs
+  // Parts of a strip that hold columns when it is cut in J (all J for the GLM-5
+  // widths, fewer for outputs narrower than a strip).
+  auto parts = [&](int J) {
+    const int swj = SW / J;
+    return (min(n_out, SW) + swj - 1) / swj;
+  };
   int J = 1;
-  while (J < 32 && passes * J * 2 <= blocks) J *= 2;
-  const int64_t units = passes * J;
+  while (J < 32 && passes * parts(J * 2) <= blocks) J *= 2;
+  const int jv = parts(J);
+  const int64_t units = passes * jv;
   for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
-    const int64_t ps = u / J;
-    const int q = (int)(ps % strips) * J + (int)(u % J);  // column part within the pass
+    const int64_t ps = u / jv;
+    const int q = (int)(ps % strips) * J + (int)(u % jv);  // column part within the pass
     int ai = 0;
     const RsItem it = rs_item<true>(g, s_pass, n_active, 1, ps / strips, &ai);
     if (it.mt == 1) cols_unit<T, GU, 1>(g, A, Wall, out, it, q, J, s_red);
