@@ -15,13 +15,16 @@
 // silu(gate) * up ("GLM-5 · Input features", excerpt mlp: the SwiGLU form).
 // Wider outputs take several strips of that many columns.  The few token
 // activations are the same for every lane (scalar loads) and the products are
-// fp32 FMAs kept in registers: no LDS and no reduction across lanes.
+// v_dot2c_f32_bf16 on row pairs (fp32 FMAs for fp32 weights) kept in registers:
+// no LDS and no reduction across lanes.
 //
 // Balance.  The launch's work is the list of items (active expert i, pass p,
 // strip s) in that order, a pass being up to kStreamMaxMT of the expert's tokens,
-// each item cut into K / kRsChunk chunks of kRsChunk weight rows.  When the items
-// fill at least half of the resident blocks, blocks take whole items (RsGeom).
-// Otherwise the P resident blocks split the chunk list into equal contiguous
+// each item cut into K / kRsChunk chunks of kRsChunk weight rows.  Calls whose
+// items fill at most half of the resident blocks (known on the host from T * k)
+// take the column split below instead.  When the items fill at least half of the
+// resident blocks, blocks take whole items (RsGeom).  Otherwise (more items than
+// resident blocks) the P resident blocks split the chunk list into equal contiguous
 // ranges, lo(b) = floor(b * total / P), so every block reads the same number of
 // weight bytes and the launch ends without a tail of lone blocks (the Stream-K
 // decomposition of Osama et al., 2023, applied to a memory-bound product).  An item whose chunks
