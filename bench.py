@@ -445,7 +445,7 @@ def measure_configs(cfg, tin, steps, names=("glm5_prefill_zipf", "mid_prefill"))
     return out
 
 
-def measure_sweep(cfg, tin, steps, warmup, tokens=(1, 8, 16, 32, 128, 256),
+def measure_sweep(cfg, tin, steps, warmup, tokens=(1, 2, 4, 8, 16, 32, 128, 256),
                   fused_tokens=(1, 8, 64)):
     """The MoE block at other batch sizes on the same weights (decode-sized batches use
     the streaming kernels): ms per step, tokens/s and the gate_up kernel's HBM rate;
@@ -462,6 +462,7 @@ def measure_sweep(cfg, tin, steps, warmup, tokens=(1, 8, 16, 32, 128, 256),
         t2["corr_bias"] = torch.from_numpy(sm["corr_bias"]).cuda()
         r = run_workload(c, t2, steps, warmup)
         out["T%d" % T] = {"tokens": T, "ms_per_step": round(r["ms_per_step"], 4),
+                          "ms_per_step_median": round(r["ms_per_step_median"], 4),
                           "tokens_per_s": round(r["value"], 1),
                           "kernel_path": "stream" if r["path"] == 1 else "mfma",
                           "gate_up_ms": r["roofline"]["kernel_ms"],
