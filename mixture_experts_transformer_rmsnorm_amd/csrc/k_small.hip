@@ -7,6 +7,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "dev_rowdot.h"
 #include "dev_small.h"
 #include "kernels.h"
 
@@ -191,14 +192,20 @@ hipError_t launch_topk(const float* logit_part, int splits, const float* corr_bi
 
 // Router selection for small batches: one block of 256 threads per token.  The
 // four wavefronts add the split-K partial logits of the splits z = w, w + 4, ...;
-// wave 0 adds the four sums in order and selects (topk_select).
+// wave 0 adds the four sums in order and selects (topk_select).  Blocks T and up
+// compute the shared expert's act_s when sh.T > 0 (dev_rowdot.h).
 template <int Q>
 __global__ __launch_bounds__(256) void topk_small_kernel(const float* __restrict__ part, int splits,
                                                          const float* __restrict__ bias, int64_t T,
                                                          int E, int k, float rs,
                                                          int32_t* __restrict__ idx_out,
-                                                         float* __restrict__ w_out) {
+                                                         float* __restrict__ w_out, SharedSmall sh) {
   __shared__ float red[4][kWave * Q];
+  __shared__ float s_rd[kRdGroupLds];
+  if (blockIdx.x >= T) {
+    shared_gate_up_block(sh, (int)(blockIdx.x - T), sh.blocks, s_rd);
+    return;
+  }
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int64_t t = blockIdx.x;
   const int64_t zstride = T * (int64_t)E;
@@ -232,14 +239,30 @@ __global__ __launch_bounds__(256) void topk_small_kernel(const float* __restrict
   topk_select<Q>(l, bias, t, E, k, rs, idx_out, w_out, nullptr);
 }
 
+// With the shared expert's blocks, each launch asks for more LDS than half a compute
+// unit's 160 KiB (the kernels do not use the extra), so that the dispatcher puts one
+// block on each compute unit rather than two on some and none on others.
+constexpr size_t kSharedSmallLdsHold = 96 * 1024;
+
+// Host-side check of a shared-expert descriptor for the small routing launches.
+static bool shared_small_ok(const SharedSmall& sh) {
+  if (sh.T == 0) return true;
+  return sh.T > 0 && sh.blocks > 0 && sh.blocks <= 65536 && sh.d > 0 && sh.d % 64 == 0 &&
+         sh.Is > 0 && sh.Is % 64 == 0 && sh.T <= kSharedSmallTokens &&
+         sh.h && sh.gate && sh.up && sh.down && sh.act_s && sh.y_s;
+}
+
 hipError_t launch_topk_small(const float* logit_part, int splits, const float* corr_bias,
                              int64_t T, int E, int k, float routed_scale, int32_t* topk_idx,
-                             float* topk_w, hipStream_t s) {
+                             float* topk_w, const SharedSmall& sh, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (!shared_small_ok(sh) || (sh.T > 0 && sh.T != T)) return hipErrorInvalidValue;
   const int q = (E + kWave - 1) / kWave;
-#define MOE_TOPKS(QQ)                                                                       \
-  topk_small_kernel<QQ><<<dim3((unsigned)T), 256, 0, s>>>(logit_part, splits, corr_bias, T, E, \
-                                                          k, routed_scale, topk_idx, topk_w)
+  const unsigned grid = (unsigned)T + (sh.T > 0 ? (unsigned)sh.blocks : 0u);
+  const size_t lds = sh.T > 0 ? kSharedSmallLdsHold : 0;
+#define MOE_TOPKS(QQ)                                                                      \
+  topk_small_kernel<QQ><<<dim3(grid), 256, lds, s>>>(logit_part, splits, corr_bias, T, E, k, \
+                                                     routed_scale, topk_idx, topk_w, sh)
   if (q <= 1) MOE_TOPKS(1);
   else if (q <= 2) MOE_TOPKS(2);
   else if (q <= 4) MOE_TOPKS(4);
@@ -267,17 +290,23 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 // M-tiles, pass prefix, header) from wave-level scans, and each assignment's row:
 // its expert's offset, plus the count before its segment, plus the earlier
 // assignments of the same expert inside the segment.  The same stable order as
-// the chunked scatter.
+// the chunked scatter.  Blocks 1 and up compute the shared expert's output y_s
+// when sh.T > 0 (dev_rowdot.h; their LDS is s_hist's).
 __global__ __launch_bounds__(1024) void route_small_kernel(
     const int32_t* __restrict__ topk_idx, int A, int E, int k, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, RouteHeader* __restrict__ hdr, int32_t* __restrict__ active,
     int2* __restrict__ mtiles, int32_t* __restrict__ pass_base, int32_t* __restrict__ perm_token,
-    int32_t* __restrict__ row_of) {
+    int32_t* __restrict__ row_of, SharedSmall sh) {
   constexpr int kSegs = 16;
   __shared__ int s_idx[kRouteSmallMax];
   __shared__ int s_hist[kSegs * 1024];  // [segment][expert]
   __shared__ int s_off[1024];
   __shared__ int s_wsum[kSegs][4];
+  static_assert(sizeof(s_hist) >= 4 * kRdGroupLds * sizeof(float), "row-dot LDS");
+  if (blockIdx.x > 0) {
+    shared_down_block<4>(sh, (int)blockIdx.x - 1, sh.blocks, reinterpret_cast<float*>(s_hist));
+    return;
+  }
   const int e = threadIdx.x, lane = e & (kWave - 1), w = e / kWave;
   const int seg = (A + kSegs - 1) / kSegs;  // assignments per segment
   for (int i = e; i < kSegs * E; i += 1024) s_hist[i] = 0;
@@ -348,11 +377,14 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
 hipError_t launch_route_small(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* counts,
                               int32_t* offsets, RouteHeader* hdr, int32_t* active, int2* mtiles,
                               int32_t* pass_base, int32_t* perm_token, int32_t* row_of,
-                              hipStream_t s) {
+                              const SharedSmall& sh, hipStream_t s) {
   const int64_t A = T * k;
   if (A > kRouteSmallMax || E > 1024) return hipErrorInvalidValue;
-  route_small_kernel<<<1, 1024, 0, s>>>(topk_idx, (int)A, E, k, counts, offsets, hdr, active,
-                                        mtiles, pass_base, perm_token, row_of);
+  if (!shared_small_ok(sh) || (sh.T > 0 && sh.T != T)) return hipErrorInvalidValue;
+  const unsigned grid = 1u + (sh.T > 0 ? (unsigned)sh.blocks : 0u);
+  const size_t lds = sh.T > 0 ? kSharedSmallLdsHold - 64 * 1024 : 0;  // beside its ~78 KB
+  route_small_kernel<<<grid, 1024, lds, s>>>(topk_idx, (int)A, E, k, counts, offsets, hdr, active,
+                                           mtiles, pass_base, perm_token, row_of, sh);
   return hipGetLastError();
 }
 

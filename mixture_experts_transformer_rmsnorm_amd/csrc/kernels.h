@@ -96,17 +96,35 @@ hipError_t launch_scan(int32_t* chunk_cnt, int nchunks, int E, int32_t* counts, 
                        RouteHeader* hdr, int32_t* active, int2* mtiles, int32_t* pass_base,
                        hipStream_t s);
 
+// The shared expert of a bf16 batch of at most kSharedSmallTokens tokens, computed
+// by extra blocks of the two small-batch routing launches below: gate/up and the
+// SwiGLU beside the selection (act_s, bf16), down beside the permutation (y_s, fp32,
+// one partial-sum set for the combine).  T = 0: no shared work in those launches.
+struct bf16;
+constexpr int kSharedSmallTokens = 4;
+struct SharedSmall {
+  const bf16* h;     // [T, d]
+  const bf16* gate;  // [Is, d]
+  const bf16* up;    // [Is, d]
+  const bf16* down;  // [d, Is]
+  bf16* act_s;       // [T, Is]
+  float* y_s;        // [T, d]
+  int T, d, Is;
+  int blocks;        // extra blocks of each launch
+};
+
 // Small batches (T * k <= kRouteSmallMax, E <= 1024): selection with one block
 // per token (no chunk histograms), then the whole permutation (counts, what
-// launch_scan writes, perm_token and row_of) in one block.
+// launch_scan writes, perm_token and row_of) in one block; each launch also runs
+// sh.blocks blocks of shared-expert work when sh.T > 0.
 constexpr int kRouteSmallMax = 2048;
 hipError_t launch_topk_small(const float* logit_part, int splits, const float* corr_bias,
                              int64_t T, int E, int k, float routed_scale, int32_t* topk_idx,
-                             float* topk_w, hipStream_t s);
+                             float* topk_w, const SharedSmall& sh, hipStream_t s);
 hipError_t launch_route_small(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* counts,
                               int32_t* offsets, RouteHeader* hdr, int32_t* active, int2* mtiles,
                               int32_t* pass_base, int32_t* perm_token, int32_t* row_of,
-                              hipStream_t s);
+                              const SharedSmall& sh, hipStream_t s);
 
 hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* chunk_base,
                           const int32_t* offsets, int64_t T, int E, int k, int32_t* perm_token,

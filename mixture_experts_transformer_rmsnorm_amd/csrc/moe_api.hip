@@ -676,21 +676,33 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
       slock.unlock();
     }
   };
-  if (!mfma) fork_shared();
-  stage(kStRouter,
-        [&] { return nt(h, d, router_w, router_w, d, E, logits, E, d, rsplit); });
   // Small batches: per-token selection blocks, then the whole permutation in one
   // block; otherwise chunked selection with histograms, scans and the scatter.
   const bool small_route = T * k <= kRouteSmallMax && E <= 1024;
+  // A few bf16 tokens on the streaming path: the shared expert runs in extra blocks
+  // of those two one-block launches, on the compute units they leave idle, instead
+  // of on the side stream (whose kernels the routing launches and the routed gate_up
+  // would wait behind).
+  const bool shared_small = has_shared && !mfma && dt == kBF16 && small_route &&
+                            T <= kSharedSmallTokens;
+  SharedSmall sh{};
+  if (shared_small)
+    sh = SharedSmall{(const bf16*)h,           (const bf16*)shared_gate, (const bf16*)shared_up,
+                     (const bf16*)shared_down, (bf16*)act_s,             sh_dn,
+                     (int)T,                   d,                        Is,
+                     kComputeUnits - (int)T};
+  if (!mfma && !shared_small) fork_shared();
+  stage(kStRouter,
+        [&] { return nt(h, d, router_w, router_w, d, E, logits, E, d, rsplit); });
   stage(kStTopk, [&] {
     return small_route ? launch_topk_small(logits, rsplit.splits, corr_bias, T, E, k,
-                                           routed_scale, topk_idx, topk_w, s)
+                                           routed_scale, topk_idx, topk_w, sh, s)
                        : launch_topk(logits, rsplit.splits, corr_bias, T, E, k, routed_scale,
                                      topk_idx, topk_w, chunk_cnt, s);
   });
   stage(kStScan, [&] {
     return small_route ? launch_route_small(topk_idx, T, E, k, counts, offsets, hdr, active,
-                                            mtiles, pass_base, perm_token, row_of, s)
+                                            mtiles, pass_base, perm_token, row_of, sh, s)
                        : launch_scan(chunk_cnt, nchunks, E, counts, offsets, hdr, active, mtiles,
                                      pass_base, s);
   });
@@ -713,12 +725,12 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
     const hipError_t e2 = hipStreamWaitEvent(s, side->join, 0);
     if (err == hipSuccess) err = e2;
     slock.unlock();
-  } else if (has_shared) {
+  } else if (has_shared && !shared_small) {
     shared_branch();  // the shared expert runs in order on s
   }
   stage(kStCombine, [&] {
-    return launch_combine(dt, x, sh_dn, has_shared ? sdsplit.splits : 0, y, topk_w, row_of, T, d,
-                          k, out, s);
+    return launch_combine(dt, x, sh_dn, has_shared ? (shared_small ? 1 : sdsplit.splits) : 0, y,
+                          topk_w, row_of, T, d, k, out, s);
   });
   return err == hipSuccess ? MOE_SUCCESS : MOE_ERROR_HIP;
 }

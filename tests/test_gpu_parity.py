@@ -61,6 +61,25 @@ def test_small_bf16_both_paths(shape, path):
     _full_check(cfg, small, route, tin, path)
 
 
+@pytest.mark.parametrize("shape", [
+    dict(d=192, Is=64, I=128, E=16, k=4),      # rows of 24 vectors, most extra blocks idle
+    dict(d=640, Is=576, I=192, E=12, k=3),     # 2-3 act_s columns per block
+    dict(d=1024, Is=2048, I=256, E=32, k=8),   # 8-9 columns per block, 4 KiB down rows
+])
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_shared_expert_beside_small_routing(shape, T):
+    """Up to 4 bf16 tokens on the streaming path: the shared expert runs in extra
+    blocks of the selection and permutation launches.  act_s element-wise against
+    the oracle, then the whole output."""
+    cfg = workloads.config("tiny_fp32", dtype="bf16", T=T, **shape)
+    cfg, small, route, tin = prepare(cfg, seed=11 + T)
+    block, _ = _full_check(cfg, small, route, tin, STREAM)
+    act_s = block.buffer(moe.MOE_BUF_SHARED_ACT, T).cpu().numpy().view(np.uint16)
+    _, _, dbg = oracle_outputs(cfg, small, route, tin, np.arange(T), debug=True)
+    check_intermediate(values(act_s.reshape(T, cfg.Is), "bf16"), dbg["act_s"], "bf16", "act_s")
+    block.close()
+
+
 @pytest.mark.parametrize("path", [STREAM, MFMA])
 def test_top1_and_all_experts(path):
     for k, E in ((1, 8), (8, 8)):
