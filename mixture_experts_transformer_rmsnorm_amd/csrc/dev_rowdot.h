@@ -163,10 +163,13 @@ __device__ __forceinline__ void shared_down_rows(const SharedSmall& sh, int m0, 
 
 // Block `b` of `nb` extra blocks of 256 lanes (one wave per SIMD, registers for 3
 // or 4 vectors of 8 rows in flight: at the GLM-5 width, d = 6144, every vector of
-// the batch's rows at once): act_s columns [b Is / nb, (b + 1) Is / nb).
+// the batch's rows at once): act_s columns [col0 + b n / nb, col0 + (b + 1) n / nb)
+// of the launch's n = col1 - col0.
 __device__ __forceinline__ void shared_gate_up_block(const SharedSmall& sh, int b, int nb,
                                                      float* lds) {
-  const int c0 = (int)((int64_t)b * sh.Is / nb), c1 = (int)((int64_t)(b + 1) * sh.Is / nb);
+  const int n = sh.col1 - sh.col0;
+  const int c0 = sh.col0 + (int)((int64_t)b * n / nb);
+  const int c1 = sh.col0 + (int)((int64_t)(b + 1) * n / nb);
   const int gl = threadIdx.x;
   static_assert(kSharedSmallTokens <= 4, "token counts dispatched below");
   if (sh.T <= 1) shared_gate_up_cols<8, 1, 4>(sh, c0, c1, gl, lds);

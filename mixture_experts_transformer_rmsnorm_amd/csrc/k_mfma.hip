@@ -31,6 +31,7 @@
 
 #include "common.h"
 #include "dev_nt.h"
+#include "dev_rowdot.h"
 #include "kernels.h"
 
 namespace moe {
@@ -694,11 +695,22 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
                      : "memory", "m0");
 }
 
-__global__ __launch_bounds__(NS_THREADS) void mfma_nt_skinny_kernel(NtArgs a) {
+// SH: blocks past the product's own compute act_s columns of the shared expert
+// (dev_rowdot.h) in the ring's LDS.
+template <bool SH>
+__global__ __launch_bounds__(NS_THREADS) void mfma_nt_skinny_kernel(NtArgs a, SharedSmall sh) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[NS_STAGES * NS_STAGE_ELEMS];
+  const int n_tiles = (a.N + NS_N - 1) / NS_N;
+  if constexpr (SH) {
+    static_assert(NS_STAGES * NS_STAGE_ELEMS * 2 >= kRdGroupLds * 4, "row-dot LDS");
+    if ((int)blockIdx.x >= n_tiles * a.splits) {
+      shared_gate_up_block(sh, (int)blockIdx.x - n_tiles * a.splits, sh.blocks,
+                           reinterpret_cast<float*>(lds));
+      return;
+    }
+  }
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n_tiles = (a.N + NS_N - 1) / NS_N;
   const int n_tile = blockIdx.x % n_tiles, z = blockIdx.x / n_tiles;
   const int nkt = a.K / NS_K;
   const int kt0 = z * a.k_tiles_per_split;
@@ -818,11 +830,22 @@ hipError_t launch_mfma_nt(const NtArgs& a, hipStream_t s) {
     mfma_nt_big_kernel<kEpiStore><<<dim3((unsigned)blocks), NB_THREADS, 0, s>>>(p);
   } else if (tm == NS_M) {
     const int64_t blocks = (int64_t)((a.N + NS_N - 1) / NS_N) * a.splits;
-    mfma_nt_skinny_kernel<<<dim3((unsigned)blocks), NS_THREADS, 0, s>>>(a);
+    mfma_nt_skinny_kernel<false><<<dim3((unsigned)blocks), NS_THREADS, 0, s>>>(a, SharedSmall{});
   } else {
     dim3 grid((a.N + kNtBN - 1) / kNtBN, (a.M + kNtBM - 1) / kNtBM, a.splits);
     mfma_nt_kernel<<<grid, 256, 0, s>>>(a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_nt_shared(const NtArgs& a, const SharedSmall& sh, hipStream_t s) {
+  int tm, tn, tk;
+  mfma_nt_tile(a.M, &tm, &tn, &tk);
+  if (a.M == 0 || tm != NS_M || !shared_small_ok(sh) || (sh.T > 0 && sh.T != a.M))
+    return hipErrorInvalidValue;
+  const int64_t blocks = (int64_t)((a.N + NS_N - 1) / NS_N) * a.splits;
+  const unsigned grid = (unsigned)blocks + (sh.T > 0 ? (unsigned)sh.blocks : 0u);
+  mfma_nt_skinny_kernel<true><<<dim3(grid), NS_THREADS, 0, s>>>(a, sh);
   return hipGetLastError();
 }
 

@@ -244,14 +244,6 @@ __global__ __launch_bounds__(256) void topk_small_kernel(const float* __restrict
 // block on each compute unit rather than two on some and none on others.
 constexpr size_t kSharedSmallLdsHold = 96 * 1024;
 
-// Host-side check of a shared-expert descriptor for the small routing launches.
-static bool shared_small_ok(const SharedSmall& sh) {
-  if (sh.T == 0) return true;
-  return sh.T > 0 && sh.blocks > 0 && sh.blocks <= 65536 && sh.d > 0 && sh.d % 64 == 0 &&
-         sh.Is > 0 && sh.Is % 64 == 0 && sh.T <= kSharedSmallTokens &&
-         sh.h && sh.gate && sh.up && sh.down && sh.act_s && sh.y_s;
-}
-
 hipError_t launch_topk_small(const float* logit_part, int splits, const float* corr_bias,
                              int64_t T, int E, int k, float routed_scale, int32_t* topk_idx,
                              float* topk_w, const SharedSmall& sh, hipStream_t s) {

@@ -78,6 +78,11 @@ struct NtArgs {
   int k_tiles_per_split;  // in units of the kernel's K tile
 };
 hipError_t launch_fma_nt(int dtype, const NtArgs& a, hipStream_t s);
+// The decode-sized bf16 product (a.M <= kNtSkinnyRows) plus sh.blocks extra blocks
+// that compute act_s columns [sh.col0, sh.col1) of the shared expert (SharedSmall,
+// below).
+struct SharedSmall;
+hipError_t launch_mfma_nt_shared(const NtArgs& a, const SharedSmall& sh, hipStream_t s);
 hipError_t launch_mfma_nt(const NtArgs& a, hipStream_t s);
 // The gate/up product of a SwiGLU MLP with its epilogue fused (bf16 only, one K
 // split, at least kNtBigTile rows): B rows [0, n_split) are the gate rows (B1)
@@ -97,9 +102,10 @@ hipError_t launch_scan(int32_t* chunk_cnt, int nchunks, int E, int32_t* counts, 
                        hipStream_t s);
 
 // The shared expert of a bf16 batch of at most kSharedSmallTokens tokens, computed
-// by extra blocks of the two small-batch routing launches below: gate/up and the
-// SwiGLU beside the selection (act_s, bf16), down beside the permutation (y_s, fp32,
-// one partial-sum set for the combine).  T = 0: no shared work in those launches.
+// by extra blocks of the router product and the two small-batch routing launches
+// below: gate/up and the SwiGLU beside the router and the selection (act_s, bf16,
+// each launch a range of its columns), down beside the permutation (y_s, fp32, one
+// partial-sum set for the combine).  T = 0: no shared work in those launches.
 struct bf16;
 constexpr int kSharedSmallTokens = 4;
 struct SharedSmall {
@@ -110,8 +116,17 @@ struct SharedSmall {
   bf16* act_s;       // [T, Is]
   float* y_s;        // [T, d]
   int T, d, Is;
-  int blocks;        // extra blocks of each launch
+  int blocks;        // extra blocks of the launch
+  int col0, col1;    // act_s columns [col0, col1) of a gate/up launch
 };
+// Host-side check of a descriptor (T = 0: none).
+inline bool shared_small_ok(const SharedSmall& sh) {
+  if (sh.T == 0) return true;
+  return sh.T > 0 && sh.T <= kSharedSmallTokens && sh.blocks > 0 && sh.blocks <= 65536 &&
+         sh.d > 0 && sh.d % 64 == 0 && sh.Is > 0 && sh.Is % 64 == 0 && 0 <= sh.col0 &&
+         sh.col0 <= sh.col1 && sh.col1 <= sh.Is && sh.h && sh.gate && sh.up && sh.down &&
+         sh.act_s && sh.y_s;
+}
 
 // Small batches (T * k <= kRouteSmallMax, E <= 1024): selection with one block
 // per token (no chunk histograms), then the whole permutation (counts, what

@@ -685,24 +685,42 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   // would wait behind).
   const bool shared_small = has_shared && !mfma && dt == kBF16 && small_route &&
                             T <= kSharedSmallTokens;
-  SharedSmall sh{};
-  if (shared_small)
-    sh = SharedSmall{(const bf16*)h,           (const bf16*)shared_gate, (const bf16*)shared_up,
-                     (const bf16*)shared_down, (bf16*)act_s,             sh_dn,
-                     (int)T,                   d,                        Is,
-                     kComputeUnits - (int)T};
+  // act_s columns [0, split) beside the router product, [split, Is) beside the
+  // selection (two fifths and three fifths: at 1-4 GLM-5 tokens 0.4-0.8 % faster
+  // than a quarter or 55 %, 1-2.5 % faster than all beside the selection); the down
+  // product beside the permutation
+  SharedSmall sh_r{}, sh_t{}, sh_p{};
+  const int rblocks = (int)cdiv(E, kMfmaBN) * rsplit.splits;
+  if (shared_small) {
+    const int split = rblocks < kComputeUnits ? (int)((int64_t)Is * 2 / 5 / 8 * 8) : 0;
+    const SharedSmall base{(const bf16*)h, (const bf16*)shared_gate, (const bf16*)shared_up,
+                           (const bf16*)shared_down, (bf16*)act_s, sh_dn, (int)T, d, Is, 0, 0, 0};
+    sh_r = base;
+    sh_r.blocks = kComputeUnits - rblocks, sh_r.col0 = 0, sh_r.col1 = split;
+    if (split == 0) sh_r.T = 0;
+    sh_t = base;
+    sh_t.blocks = kComputeUnits - (int)T, sh_t.col0 = split, sh_t.col1 = Is;
+    sh_p = base;
+    sh_p.blocks = kComputeUnits - 1, sh_p.col0 = sh_p.col1 = 0;
+  }
   if (!mfma && !shared_small) fork_shared();
-  stage(kStRouter,
-        [&] { return nt(h, d, router_w, router_w, d, E, logits, E, d, rsplit); });
+  stage(kStRouter, [&] {
+    if (sh_r.T > 0) {
+      NtArgs a{h, d, router_w, router_w, d, (int)E, logits, (int)T, (int)E, (int)d,
+               rsplit.splits, rsplit.kt_per};
+      return launch_mfma_nt_shared(a, sh_r, cs);
+    }
+    return nt(h, d, router_w, router_w, d, E, logits, E, d, rsplit);
+  });
   stage(kStTopk, [&] {
     return small_route ? launch_topk_small(logits, rsplit.splits, corr_bias, T, E, k,
-                                           routed_scale, topk_idx, topk_w, sh, s)
+                                           routed_scale, topk_idx, topk_w, sh_t, s)
                        : launch_topk(logits, rsplit.splits, corr_bias, T, E, k, routed_scale,
                                      topk_idx, topk_w, chunk_cnt, s);
   });
   stage(kStScan, [&] {
     return small_route ? launch_route_small(topk_idx, T, E, k, counts, offsets, hdr, active,
-                                            mtiles, pass_base, perm_token, row_of, sh, s)
+                                            mtiles, pass_base, perm_token, row_of, sh_p, s)
                        : launch_scan(chunk_cnt, nchunks, E, counts, offsets, hdr, active, mtiles,
                                      pass_base, s);
   });

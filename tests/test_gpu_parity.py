@@ -69,8 +69,9 @@ def test_small_bf16_both_paths(shape, path):
 @pytest.mark.parametrize("T", [1, 2, 3, 4])
 def test_shared_expert_beside_small_routing(shape, T):
     """Up to 4 bf16 tokens on the streaming path: the shared expert runs in extra
-    blocks of the selection and permutation launches.  act_s element-wise against
-    the oracle, then the whole output."""
+    blocks of the router, selection and permutation launches (act_s columns split
+    between the first two).  act_s element-wise against the oracle, then the whole
+    output."""
     cfg = workloads.config("tiny_fp32", dtype="bf16", T=T, **shape)
     cfg, small, route, tin = prepare(cfg, seed=11 + T)
     block, _ = _full_check(cfg, small, route, tin, STREAM)
