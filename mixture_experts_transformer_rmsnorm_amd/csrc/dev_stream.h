@@ -177,11 +177,14 @@ __device__ __forceinline__ float dot2_bf16(uint32_t x, uint32_t y, float c) {
 // lane.  LN: the lane's ok and wcol.
 //   gate_up: A = h [T, d] (rows gathered by perm_token), W = gate_up[e] [d, 2I]
 //   down:    A = act [rows, I],                          W = down[e] [I, d]
+// A's row r is read at A + (r - row0) * lda (row0: the first row of an A that
+// holds only the item's rows).
 template <typename T, bool GU, int MT, typename LN, int RPI = rs_rows_per_step<GU>()>
 __device__ __forceinline__ void rs_accumulate(const GroupArgs& g, const T* __restrict__ A,
                                               int64_t lda, const T* __restrict__ W, int64_t ldw,
                                               const RsItem& it, const LN& ln, int k0, int k1,
-                                              int kstep, float (&acc)[MT][Elem<T>::kVec]) {
+                                              int kstep, float (&acc)[MT][Elem<T>::kVec],
+                                              int64_t row0 = 0) {
   constexpr int V = Elem<T>::kVec;
   static_assert(RPI % 8 == 0, "whole 16-byte activation vectors per step");
 #pragma unroll
@@ -195,7 +198,7 @@ __device__ __forceinline__ void rs_accumulate(const GroupArgs& g, const T* __res
     const int mm = m < it.mt ? m : it.mt - 1;  // rows past mt repeat the last one, never stored
     const int64_t prow = it.seg + it.m0 + mm;
     const int64_t r = GU ? (int64_t)g.perm_token[prow] : prow;
-    arow[m] = A + r * lda;
+    arow[m] = A + (r - row0) * lda;
   }
   const T* wp = W + (int64_t)k0 * ldw + ln.wcol;
   for (int k = k0; k < k1; k += kstep, wp += (int64_t)kstep * ldw) {

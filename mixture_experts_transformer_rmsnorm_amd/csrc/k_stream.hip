@@ -84,18 +84,52 @@ __global__ __launch_bounds__(kWave) void stream_fixup_kernel(GroupArgs g, Stream
 // lanes; a lane reads runs of RPI consecutive rows, J * RPI rows apart, over the
 // part's columns (gate_up: the first half of a group's lanes read gate and the
 // second half the matching up columns), and the J groups' sums meet in LDS, one
-// token row at a time, for the epilogue.  At one token (8 passes, J = 32) a
-// gate_up unit reads 128 bytes of gate and 128 of up columns per weight row, a
-// down unit 384 bytes.
+// token row at a time, for the epilogue.  A down unit at one token (8 passes,
+// J = 32) reads 384 bytes per weight row.  The gate_up would read 128 bytes of gate
+// and 128 of up columns per row at J = 32, so where J would exceed 8 it splits K
+// instead (gu_ksplit below): J = 8 parts times S row ranges per pass, 512-byte runs
+// per row at the GLM-5 width; each unit leaves fp32 gate and up sums of its range,
+// and each down unit first forms its pass's act rows from those sums (silu of the
+// gate sum times the up sum, rounded to D, as the gate_up epilogue otherwise does)
+// in LDS.  At one token the gate_up launch takes 62-63 us instead of 70, the down
+// launch 2-3 us longer.
 struct ColLane {
   bool ok, is_up;
   int64_t wcol;
 };
 
+// K split of the gate_up for the fewest passes (ColKSplit).  When `pairs` (pass,
+// strip) pairs of the gate_up over `blocks` blocks would cut each strip into more
+// than 8 column parts, it cuts it into 8 parts times S row ranges, S the largest
+// power of two up to 8 with pairs * parts * S <= blocks: each unit then reads
+// 512-byte runs of gate and of up columns per weight row at the GLM-5 width (128
+// bytes at 32 parts), which stream faster.  Returns S, or 0 for no split.  The
+// down launch evaluates the same function on the gate_up's geometry.
+template <typename T>
+__device__ __forceinline__ int gu_ksplit(int64_t pairs, int blocks, int I) {
+  constexpr int SW = rs_strip_cols<T, true, rs_threads<true>()>();
+  auto parts = [&](int J) {
+    const int swj = SW / J;
+    return (min(I, SW) + swj - 1) / swj;
+  };
+  if (pairs * parts(16) > blocks) return 0;
+  int S = 1;
+  while (S < 8 && pairs * parts(8) * S * 2 <= blocks) S *= 2;
+  return S >= 2 ? S : 0;
+}
+
+// A unit's share of the K split: S ranges (0: none), this gate_up unit's range s.
+struct ColKs {
+  float* part;  // [S][rows][2I]
+  int64_t rows;
+  int S, s;
+};
+
 template <typename T, bool GU, int MT>
 __device__ __forceinline__ void cols_unit(const GroupArgs& g, const T* __restrict__ A,
                                           const T* __restrict__ Wall, T* __restrict__ out,
-                                          const RsItem& it, int q, int J, float* s_red) {
+                                          const RsItem& it, int q, int J, float* s_red,
+                                          const ColKs& kc, T* act, T* s_act) {
   // 8 rows in flight per lane for both products: the down blocks' 768 lanes leave
   // at most 168 registers per lane, too few for 16 rows and 8 token rows
   constexpr int NTH = rs_threads<GU>(), V = Elem<T>::kVec, RPI = 8;
@@ -104,6 +138,49 @@ __device__ __forceinline__ void cols_unit(const GroupArgs& g, const T* __restric
   const int LPR = NTH / J;                     // lanes per weight row
   const int SWJ = (GU ? LPR / 2 : LPR) * V;    // output columns of a part
   const int tid = threadIdx.x, rg = tid / LPR, cl = tid % LPR;
+  const int64_t row0 = it.seg + it.m0;         // the item's first permuted row
+  int kb = 0, ke = K;
+  int64_t a_row0 = 0;
+  if (GU && kc.S) {
+    kb = kc.s * (K / kc.S);
+    ke = kb + K / kc.S;
+  }
+  if (!GU && kc.S) {
+    // act of the item's rows from the gate_up's range sums, rounded to D as the
+    // gate_up epilogue rounds it, into LDS; the first column part also stores it
+    // (4 consecutive columns per lane and pass of the loop, every range's loads
+    // issued before the sums)
+    const int I = g.I, I4 = I / 4;
+    for (int i = tid; i < it.mt * I4; i += NTH) {
+      const int m = i / I4, c = (i % I4) * 4;
+      float4 gv[8], uv[8];
+#pragma unroll
+      for (int z = 0; z < 8; ++z) {
+        if (z < kc.S) {
+          const float* p = kc.part + ((int64_t)z * kc.rows + row0 + m) * 2 * I + c;
+          gv[z] = *reinterpret_cast<const float4*>(p);
+          uv[z] = *reinterpret_cast<const float4*>(p + I);
+        }
+      }
+      float gs[4] = {0.f, 0.f, 0.f, 0.f}, us[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int z = 0; z < 8; ++z) {
+        if (z < kc.S) {
+          gs[0] += gv[z].x; gs[1] += gv[z].y; gs[2] += gv[z].z; gs[3] += gv[z].w;
+          us[0] += uv[z].x; us[1] += uv[z].y; us[2] += uv[z].z; us[3] += uv[z].w;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float v = silu(gs[j]) * us[j];
+        Elem<T>::store1(s_act + m * I + c + j, v);
+        if (q == 0) Elem<T>::store1(act + (row0 + m) * I + c + j, v);
+      }
+    }
+    __syncthreads();
+    A = s_act;
+    a_row0 = row0;
+  }
   ColLane ln;
   ln.is_up = GU && cl >= LPR / 2;
   const int ocol = q * SWJ + (GU ? cl % (LPR / 2) : cl) * V;
@@ -111,7 +188,7 @@ __device__ __forceinline__ void cols_unit(const GroupArgs& g, const T* __restric
   ln.wcol = (ln.is_up ? (int64_t)g.I : 0) + ocol;
   float acc[MT][V];
   rs_accumulate<T, GU, MT, ColLane, RPI>(g, A, K, Wall + (int64_t)it.e * K * ldw, ldw, it, ln,
-                                         rg * RPI, K, J * RPI, acc);
+                                         kb + rg * RPI, ke, J * RPI, acc, a_row0);
   // s_red[rg][cl * V + c]: a row group's sums, gate columns first (for gate_up)
   const int vals = LPR * V;
 #pragma unroll
@@ -120,7 +197,8 @@ __device__ __forceinline__ void cols_unit(const GroupArgs& g, const T* __restric
 #pragma unroll
     for (int c = 0; c < V; ++c) s_red[tid * V + c] = acc[m][c];
     __syncthreads();
-    T* orow = out + (int64_t)(it.seg + it.m0 + m) * n_out;
+    T* orow = out + (row0 + m) * n_out;
+    float* prow = GU && kc.S ? kc.part + ((int64_t)kc.s * kc.rows + row0 + m) * 2 * g.I : nullptr;
     for (int t = tid; t < SWJ; t += NTH) {
       float a = 0.f, u = 0.f;
       for (int r = 0; r < J; ++r) {
@@ -128,20 +206,33 @@ __device__ __forceinline__ void cols_unit(const GroupArgs& g, const T* __restric
         if (GU) u += s_red[r * vals + SWJ + t];
       }
       const int col = q * SWJ + t;
-      if (col < n_out) Elem<T>::store1(orow + col, GU ? silu(a) * u : a);
+      if (col < n_out) {
+        if (GU && kc.S) {
+          prow[col] = a;
+          prow[g.I + col] = u;
+        } else {
+          Elem<T>::store1(orow + col, GU ? silu(a) * u : a);
+        }
+      }
     }
     __syncthreads();
   }
 }
 
+// gu_blocks: the blocks of the gate_up launch (the down launch uses them to see
+// whether the gate_up split K).  act: for the down launch, its activation rows
+// (A itself), which it stores when it forms them from the K split's sums; A is
+// then never read.
 template <typename T, bool GU>
 __global__ __launch_bounds__(rs_threads<GU>()) void stream_cols_kernel(GroupArgs g, int blocks,
-                                                                       const T* __restrict__ A,
+                                                                       ColKSplit ks, int gu_blocks,
+                                                                       const T* A, T* act,
                                                                        const T* __restrict__ Wall,
                                                                        T* __restrict__ out) {
   constexpr int NTH = rs_threads<GU>(), V = Elem<T>::kVec;
   __shared__ int s_pass[kMaxStreamExperts + 1];
   __shared__ float s_red[NTH * V];
+  extern __shared__ uint4 s_dyn[];  // kRsLdsHold bytes: the down units' act rows
   const int n_active = g.hdr->n_active;
   for (int i = threadIdx.x; i <= n_active; i += NTH) s_pass[i] = g.pass_base[i];
   __syncthreads();
@@ -155,19 +246,32 @@ __global__ __launch_bounds__(rs_threads<GU>()) void stream_cols_kernel(GroupArgs
     const int swj = SW / J;
     return (min(n_out, SW) + swj - 1) / swj;
   };
+  ColKs kc{ks.part, ks.rows, 0, 0};
+  if (ks.ok) {
+    constexpr int SWG = rs_strip_cols<T, true, rs_threads<true>()>();
+    kc.S = gu_ksplit<T>((int64_t)s_pass[n_active] * ((g.I + SWG - 1) / SWG), gu_blocks, g.I);
+  }
   int J = 1;
-  while (J < 32 && passes * parts(J * 2) <= blocks) J *= 2;
+  if (GU && kc.S) {
+    J = 8;
+  } else {
+    while (J < 32 && passes * parts(J * 2) <= blocks) J *= 2;
+  }
   const int jv = parts(J);
-  const int64_t units = passes * jv;
+  const int S = GU && kc.S ? kc.S : 1;
+  const int64_t units = passes * jv * S;
+  T* s_act = reinterpret_cast<T*>(s_dyn);
   for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
-    const int64_t ps = u / jv;
-    const int q = (int)(ps % strips) * J + (int)(u % jv);  // column part within the pass
+    kc.s = (int)(u % S);
+    const int64_t ur = u / S;
+    const int64_t ps = ur / jv;
+    const int q = (int)(ps % strips) * J + (int)(ur % jv);  // column part within the pass
     int ai = 0;
     const RsItem it = rs_item<true>(g, s_pass, n_active, 1, ps / strips, &ai);
-    if (it.mt == 1) cols_unit<T, GU, 1>(g, A, Wall, out, it, q, J, s_red);
-    else if (it.mt == 2) cols_unit<T, GU, 2>(g, A, Wall, out, it, q, J, s_red);
-    else if (it.mt <= 4) cols_unit<T, GU, 4>(g, A, Wall, out, it, q, J, s_red);
-    else cols_unit<T, GU, 8>(g, A, Wall, out, it, q, J, s_red);
+    if (it.mt == 1) cols_unit<T, GU, 1>(g, A, Wall, out, it, q, J, s_red, kc, act, s_act);
+    else if (it.mt == 2) cols_unit<T, GU, 2>(g, A, Wall, out, it, q, J, s_red, kc, act, s_act);
+    else if (it.mt <= 4) cols_unit<T, GU, 4>(g, A, Wall, out, it, q, J, s_red, kc, act, s_act);
+    else cols_unit<T, GU, 8>(g, A, Wall, out, it, q, J, s_red, kc, act, s_act);
   }
 }
 
@@ -200,19 +304,38 @@ static hipError_t resident_blocks(int* blocks) {
   return hipSuccess;
 }
 
+// Whether the GU product of a call with at most max_passes passes runs the column
+// split on `blocks` resident blocks: J >= 2 whatever the routing.
+template <typename T, bool GU>
+static bool col_mode(const GroupArgs& g, int64_t max_passes, int blocks) {
+  constexpr int SW = rs_strip_cols<T, GU, rs_threads<GU>()>();
+  const int64_t strips = ((GU ? g.I : g.d) + SW - 1) / SW;
+  return 2 * max_passes * strips <= blocks;
+}
+
 template <typename T, bool GU>
 static hipError_t launch_stream(const GroupArgs& g, const StreamFix& fx_in, int64_t max_passes,
-                                const void* A, const void* W, void* out, hipStream_t s) {
+                                const ColKSplit& ks_in, const void* A, const void* W, void* out,
+                                hipStream_t s) {
   StreamFix fx = fx_in;
   hipError_t err = resident_blocks<T, GU>(&fx.blocks);
   if (err != hipSuccess) return err;
   if (fx.blocks < 1 || fx.blocks > kStreamMaxBlocks || g.E > kMaxStreamExperts)
     return hipErrorInvalidValue;
-  constexpr int SW = rs_strip_cols<T, GU, rs_threads<GU>()>();
-  const int64_t strips = ((GU ? g.I : g.d) + SW - 1) / SW;
-  if (2 * max_passes * strips <= fx.blocks) {  // J >= 2 whatever the routing
+  if (col_mode<T, GU>(g, max_passes, fx.blocks)) {
+    // The K split is allowed only when both products run the column split (the down
+    // units form act) and a unit's act rows fit the LDS the launch holds anyway;
+    // both launches decide it alike.
+    int gu_blocks = 0, dn_blocks = 0;
+    err = resident_blocks<T, true>(&gu_blocks);
+    if (err == hipSuccess) err = resident_blocks<T, false>(&dn_blocks);
+    if (err != hipSuccess) return err;
+    ColKSplit ks = ks_in;
+    ks.ok = ks.ok && ks.part && col_mode<T, true>(g, max_passes, gu_blocks) &&
+            col_mode<T, false>(g, max_passes, dn_blocks) &&
+            (size_t)kStreamMaxMT * g.I * sizeof(T) <= kRsLdsHold;
     stream_cols_kernel<T, GU><<<dim3((unsigned)fx.blocks), rs_threads<GU>(), kRsLdsHold, s>>>(
-        g, fx.blocks, (const T*)A, (const T*)W, (T*)out);
+        g, fx.blocks, ks, gu_blocks, (const T*)A, GU ? nullptr : (T*)A, (const T*)W, (T*)out);
     return hipGetLastError();
   }
   stream_kernel<T, GU><<<dim3((unsigned)fx.blocks), rs_threads<GU>(), kRsLdsHold, s>>>(
@@ -225,17 +348,17 @@ static hipError_t launch_stream(const GroupArgs& g, const StreamFix& fx_in, int6
 }
 
 hipError_t launch_stream_gate_up(int dtype, const GroupArgs& g, const StreamFix& fx,
-                                 int64_t max_passes, const void* h, const void* gate_up,
-                                 void* act, hipStream_t s) {
-  if (dtype == kBF16) return launch_stream<bf16, true>(g, fx, max_passes, h, gate_up, act, s);
-  return launch_stream<float, true>(g, fx, max_passes, h, gate_up, act, s);
+                                 int64_t max_passes, const ColKSplit& ks, const void* h,
+                                 const void* gate_up, void* act, hipStream_t s) {
+  if (dtype == kBF16) return launch_stream<bf16, true>(g, fx, max_passes, ks, h, gate_up, act, s);
+  return launch_stream<float, true>(g, fx, max_passes, ks, h, gate_up, act, s);
 }
 
 hipError_t launch_stream_down(int dtype, const GroupArgs& g, const StreamFix& fx,
-                              int64_t max_passes, const void* act, const void* down, void* y,
-                              hipStream_t s) {
-  if (dtype == kBF16) return launch_stream<bf16, false>(g, fx, max_passes, act, down, y, s);
-  return launch_stream<float, false>(g, fx, max_passes, act, down, y, s);
+                              int64_t max_passes, const ColKSplit& ks, void* act,
+                              const void* down, void* y, hipStream_t s) {
+  if (dtype == kBF16) return launch_stream<bf16, false>(g, fx, max_passes, ks, act, down, y, s);
+  return launch_stream<float, false>(g, fx, max_passes, ks, act, down, y, s);
 }
 
 }  // namespace moe

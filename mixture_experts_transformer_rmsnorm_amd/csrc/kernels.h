@@ -189,16 +189,29 @@ struct StreamFix {
   int blocks;           // set by the launcher: resident blocks, at most kStreamMaxBlocks
 };
 
+// K split of the column-split gate_up for the fewest passes: when allowed (ok) and
+// the passes would cut each row into more than 8 column parts, the gate_up launch
+// instead cuts each pass into 8 column parts times S row ranges and leaves fp32
+// gate and up sums per range in part ([S][rows][2I], rows = the call's permuted
+// rows); the down launch then forms act = D(silu(sum gate) * sum up) from them.
+struct ColKSplit {
+  float* part;
+  int64_t rows;
+  bool ok;
+};
+// fp32 words the K split needs for `rows` permuted rows (S <= 8 ranges).
+inline int64_t col_ksplit_floats(int64_t rows, int I) { return 8 * rows * 2 * (int64_t)I; }
+
 // act[row][n] = D(silu(h[tok] . G[:, n]) * (h[tok] . G[:, I + n]))  for every permuted row.
 // max_passes: an upper bound of the call's streaming passes (T * k); when it fits
 // the resident blocks the column split runs (no partial sums, no fixup).
 hipError_t launch_stream_gate_up(int dtype, const GroupArgs& g, const StreamFix& fx,
-                                 int64_t max_passes, const void* h, const void* gate_up,
-                                 void* act, hipStream_t s);
+                                 int64_t max_passes, const ColKSplit& ks, const void* h,
+                                 const void* gate_up, void* act, hipStream_t s);
 // y[row][c] = D(act[row] . down[e][:, c])
 hipError_t launch_stream_down(int dtype, const GroupArgs& g, const StreamFix& fx,
-                              int64_t max_passes, const void* act, const void* down, void* y,
-                              hipStream_t s);
+                              int64_t max_passes, const ColKSplit& ks, void* act,
+                              const void* down, void* y, hipStream_t s);
 
 // rows: T * k, the permuted rows of the call (it picks the weight loads' cache policy)
 hipError_t launch_mfma_gate_up(const GroupArgs& g, int max_mtiles, int64_t rows, const void* h,

@@ -730,14 +730,18 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
     });
   GroupArgs g{counts, offsets, hdr, active, mtiles, perm_token, pass_base, E, d, I};
   const StreamFix fx{s_parts, stream_slot_floats(dt, I, d), 0};
+  // the gate_up's K split keeps its range sums in the streaming part-sum region
+  const ColKSplit ks{s_parts, A,
+                     L.s_parts != 0 && col_ksplit_floats(A, I) <=
+                                           (int64_t)kStreamMaxBlocks * 2 * fx.slot_floats};
   const int max_mtiles = (int)(cdiv(A, kGroupBM) + std::min<int64_t>(E, A));
   stage(kStGateUp, [&] {
     return mfma ? launch_mfma_gate_up(g, max_mtiles, A, h, gate_up, act, s)
-                : launch_stream_gate_up(dt, g, fx, A, h, gate_up, act, s);
+                : launch_stream_gate_up(dt, g, fx, A, ks, h, gate_up, act, s);
   });
   stage(kStDown, [&] {
     return mfma ? launch_mfma_down(g, max_mtiles, act, down, y, s)
-                : launch_stream_down(dt, g, fx, A, act, down, y, s);
+                : launch_stream_down(dt, g, fx, A, ks, act, down, y, s);
   });
   if (side) {
     const hipError_t e2 = hipStreamWaitEvent(s, side->join, 0);

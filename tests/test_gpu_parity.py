@@ -81,6 +81,17 @@ def test_shared_expert_beside_small_routing(shape, T):
     block.close()
 
 
+@pytest.mark.parametrize("T", [1, 2, 5])
+def test_fp32_smallest_batches(T):
+    """fp32 at 1, 2 and 5 tokens on the streaming path: the gate_up splits its
+    weight rows into ranges whose sums the down launch adds (1 and 2 tokens), and
+    the side-stream shared expert (fp32 plans keep it there)."""
+    cfg = workloads.config("tiny_fp32", T=T)
+    cfg, small, route, tin = prepare(cfg, seed=21 + T)
+    block, _ = _full_check(cfg, small, route, tin, STREAM)
+    block.close()
+
+
 @pytest.mark.parametrize("path", [STREAM, MFMA])
 def test_top1_and_all_experts(path):
     for k, E in ((1, 8), (8, 8)):
