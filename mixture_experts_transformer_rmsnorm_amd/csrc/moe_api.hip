@@ -680,9 +680,9 @@ moe_status_t moe_block_forward(moe_plan_t p, void* workspace, size_t workspace_b
   // block; otherwise chunked selection with histograms, scans and the scatter.
   const bool small_route = T * k <= kRouteSmallMax && E <= 1024;
   // A few bf16 tokens on the streaming path: the shared expert runs in extra blocks
-  // of those two one-block launches, on the compute units they leave idle, instead
-  // of on the side stream (whose kernels the routing launches and the routed gate_up
-  // would wait behind).
+  // of the router's split-K product and of those two one-block launches, on the
+  // compute units they leave idle, instead of on the side stream (whose kernels the
+  // routing launches and the routed gate_up would wait behind).
   const bool shared_small = has_shared && !mfma && dt == kBF16 && small_route &&
                             T <= kSharedSmallTokens;
   // act_s columns [0, split) beside the router product, [split, Is) beside the
