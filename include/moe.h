@@ -51,9 +51,11 @@
  *    path is not MFMA also owns one non-blocking side stream and two events on
  *    the device current at moe_plan_create (made there, released by
  *    moe_plan_destroy; a forward call creates no HIP object): on the STREAM path
- *    the shared expert runs there, forked from and joined back to the call's
- *    stream, so the call stays ordered on its stream (and can be captured into
- *    a graph); calls on another device run it in order on their own stream.
+ *    from 5 tokens (and for fp32 plans) the shared expert runs there, forked from
+ *    and joined back to the call's stream, so the call stays ordered on its
+ *    stream (and can be captured into a graph); calls on another device run it in
+ *    order on their own stream.  At 1-4 bf16 tokens it runs inside the router,
+ *    selection and permutation launches on the call's stream.
  *    Concurrent calls on one plan serialise only their host-side enqueueing.
  *    A workspace serves one call in flight at a time; later calls on the same
  *    stream may reuse it.
@@ -329,7 +331,9 @@ MOE_API int32_t moe_plan_path(moe_plan_t plan, int64_t num_tokens, int32_t top_k
  * while too few are left is neither timed nor counted.  A stage whose work another stage's kernel does
  * records nothing: bf16 shared_act when the shared (or dense) gate/up product
  * runs at 256 rows or more in one K split and forms silu(gate) * up itself
- * (its time is in shared_gate_up).  Timing state is the only mutable part of a
+ * (its time is in shared_gate_up); the three shared-expert stages at 1-4 bf16
+ * tokens on the STREAM path (their time is in router_logits, router_topk and
+ * permute_scan).  Timing state is the only mutable part of a
  * plan and is meant for one thread. */
 #define MOE_MAX_STAGES 16
 MOE_API moe_status_t moe_set_stage_timing(moe_plan_t plan, int32_t stage_mask);
