@@ -67,9 +67,12 @@ struct Split {
 // at least two K tiles per split and at most max_splits partial sums for the
 // consumer to add.  The 128-row kernel asks for about kTargetBlocks blocks.  The
 // 256-row kernel holds a compute unit alone: with fewer tiles than compute
-// units it splits K to fill one wave of them, with more it does not split (the
-// partial sums cost HBM traffic twice, in the product and in its consumer: a
-// 384-tile product split in two fills its last wave but the step is slower).
+// units it splits K to fill one wave of them.  With more it splits only a deep
+// product (K of 128 tiles or more) whose last wave would be at most half full, in
+// two: the partial sums cost HBM traffic twice, in the product and in its
+// consumer.  (A 384-tile product split in two fills its last wave: at K = 12288,
+// the dense block's down product at 4096 tokens, the block is 1.7 % faster; at
+// K = 2048, the MoE block's shared down product, the step is slower.)
 // The 64-row kernel, one block per compute unit too and bound by its weight
 // stream, takes the split count with the fewest K-steps on the busiest of `cus`
 // compute units, a split's partial sums (M x 128 fp32 per tile, written and read
@@ -81,7 +84,11 @@ Split nt_split(int64_t M, int64_t N, int64_t K, int tm, int tn, int tk, int max_
   const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(max_splits, nkt / 2));
   int64_t s = 1;
   if (tm == kNtBigTile) {
-    if (tiles < kComputeUnits) s = std::min<int64_t>(smax, cdiv(kComputeUnits, tiles));
+    if (tiles < kComputeUnits)
+      s = std::min<int64_t>(smax, cdiv(kComputeUnits, tiles));
+    else if (nkt >= 128 && tiles % kComputeUnits != 0 &&
+             tiles % kComputeUnits <= kComputeUnits / 2)
+      s = std::min<int64_t>(smax, 2);
   } else if (tm == kNtSkinnyRows) {
     double best = 0.0;
     for (int64_t c = 1; c <= smax; ++c) {
