@@ -470,6 +470,10 @@ def measure_sweep(cfg, tin, steps, warmup, tokens=(1, 2, 4, 8, 16, 32, 128, 256)
                               r["roofline"]["achieved"],
                           "gate_up_frac": r["roofline"]["frac"],
                           "active_experts": r["roofline"]["active_experts"]}
+        if T <= 8:
+            # per-stage breakdown (a separate pass with every stage between HIP events;
+            # a stage whose work another stage's launch does is absent)
+            out["T%d" % T]["stage_ms"] = r["stage_ms"]
         log("sweep T=%d: %.4f ms/step, %.1f tokens/s" % (T, r["ms_per_step"], r["value"]))
         del t2
     import mixture_experts_transformer_rmsnorm_amd as moe
