@@ -61,11 +61,13 @@ def dense_forward(inp):
     routed = np.einsum("te,ted->td", mask, Y)
 
     shared = np.zeros_like(x)
+    act_s = None
     if inp.get("shared_gate") is not None:
         sg, su, sd = (_val(inp[n], dt) for n in ("shared_gate", "shared_up", "shared_down"))
         gs, us = h @ sg.T, h @ su.T
-        shared = (gs / (1.0 + np.exp(-gs)) * us) @ sd.T
+        act_s = gs / (1.0 + np.exp(-gs)) * us
+        shared = act_s @ sd.T
     delta = shared + routed
     out = _rnd((x + delta).astype(np.float32), dt)
     return dict(h=h, logits=logits, scores=s, key=key, idx=idx, w=w, delta=delta, out=out,
-                Y=Y, act=a)
+                Y=Y, act=a, act_s=act_s, shared=shared)

@@ -234,6 +234,12 @@ def test_oracle_matches_dense_bruteforce(name, overrides, seed):
     # per-assignment expert outputs against the dense evaluation
     Yd = np.take_along_axis(b["Y"], b["idx"][:, :, None], axis=1)
     np.testing.assert_allclose(r["debug"]["y"], Yd, rtol=1e-9, atol=1e-12)
+    Ad = np.take_along_axis(b["act"], b["idx"][:, :, None], axis=1)
+    np.testing.assert_allclose(r["debug"]["act"], Ad, rtol=1e-9, atol=1e-12)
+    if cfg.Is > 0:
+        # the shared expert's activation and output (debug outputs the GPU tests use)
+        np.testing.assert_allclose(r["debug"]["act_s"], b["act_s"], rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(r["debug"]["s"], b["shared"], rtol=1e-9, atol=1e-12)
     assert np.array_equal(r["out"], b["out"])
 
 
