@@ -191,13 +191,14 @@ def test_plan_for_more_tokens_than_the_call(path, max_tokens, calls):
     block.close()
 
 
-@pytest.mark.parametrize("path", [STREAM, MFMA])
-def test_first_call_captured_in_a_graph(path):
+@pytest.mark.parametrize("path,T", [(STREAM, 64), (MFMA, 64), (STREAM, 1), (STREAM, 3)])
+def test_first_call_captured_in_a_graph(path, T):
     """A forward call creates no HIP object (the side stream of the shared expert and
     its events come from plan creation), so even a plan's first call can be captured
     into a graph.  Each replay, with eager calls and synchronisations between them,
-    must equal an uncaptured call bit for bit."""
-    cfg = workloads.config("tiny_fp32", dtype="bf16", T=64, d=512, E=16, I=256, Is=256, k=4)
+    must equal an uncaptured call bit for bit.  At 1 and 3 tokens the shared expert
+    runs inside the routing launches and (at 1) the gate_up splits K."""
+    cfg = workloads.config("tiny_fp32", dtype="bf16", T=T, d=512, E=16, I=256, Is=256, k=4)
     cfg, small, route, tin = prepare(cfg, seed=23)
     ref_block, ref = run_gpu(cfg, tin, path)
     block = make_block(cfg, tin, path)
