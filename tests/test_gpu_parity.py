@@ -118,8 +118,11 @@ def test_zero_tokens_is_a_noop():
     assert torch.all(sentinel == 7.0)
 
 
-def test_out_aliases_x_and_repeatability():
-    cfg, small, route, tin = prepare(workloads.config("tiny_fp32", dtype="bf16", T=200, E=16,
+@pytest.mark.parametrize("T", [200, 1])
+def test_out_aliases_x_and_repeatability(T):
+    """Bitwise repeatability and in-place calls; at 1 token on the streaming path the
+    shared expert's row sums and the gate_up's row-range sums take part."""
+    cfg, small, route, tin = prepare(workloads.config("tiny_fp32", dtype="bf16", T=T, E=16,
                                                       k=4, d=256, I=128, Is=128))
     for path in (STREAM, MFMA):
         block, out1 = run_gpu(cfg, tin, path)
